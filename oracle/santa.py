@@ -1,0 +1,371 @@
+"""SANTA++ sampled-team decode attention, step by step, in float64 on the CPU.
+
+TEST INFRASTRUCTURE (see the package docstring): the plain, slow reference the
+HIP path is compared with. It shares no code with that path.
+
+What the method computes ([ABS]; [EXP] section 三 "核心方法"): cached keys are
+grouped into teams; the new query scores one representative key per team; a
+softmax over those scores gives team probabilities p; teams are sampled with
+those probabilities; exact attention scores are computed only inside the
+sampled teams; each team's contribution is re-weighted by the inverse of its
+inclusion probability, which makes the result an importance-sampling estimate
+of attention over the whole cache.
+
+Readings taken where the pages leave a step open (each repeated where used):
+  R1  teams are contiguous runs of T tokens, one team per KV page; the last
+      team of a sequence may be shorter ([EXP] 3.2 says the partition is open).
+  R2  the representative is the mean key of the team, stored in the KV type
+      (one round-to-nearest-even of the exact mean), unscaled ([EXP] section 三
+      lists mean / medoid / random).
+  R3  team scores and token scores carry the usual 1/sqrt(d) factor.
+  R4  "sample M teams" = M independent draws with replacement by inverse CDF,
+      then duplicates removed; inclusion probability pi = 1 - (1 - p)^M and the
+      weight is 1/pi ([ABS]: inverse of the inclusion probability; [EXP]
+      step 5 writes 1/p_i, which the abstract overrides).
+  R5  the estimate of the attention output is the ratio of the re-weighted
+      numerator sum to the re-weighted denominator sum (both sums are
+      unbiased; the ratio is consistent).
+  R6  if M >= number of teams, every team is read and pi = 1 (full coverage).
+  R7  draws are independent per query head; a KV head's G query heads share
+      nothing but the cache.
+  R8  an empty sequence (length 0) gives out = 0 and lse = -inf.
+
+Parity pins (tests/test_oracle_pins.py): dense attention against torch's
+scaled_dot_product_attention; full coverage against dense; brute-force
+enumeration of all draw sequences on tiny inputs for unbiasedness of both
+sums and for P(t in S) = pi_t; Monte Carlo convergence over seeds; the
+expected set size against its closed form; chi-square of draw frequencies
+against p; invariants (constant values, permuted page tables); team scores
+with one-token teams against the attention weights of the library routine.
+"""
+import math
+
+import numpy as np
+
+from .numerics import decode, round_to_dtype
+from .philox import draw_words, word_to_uniform
+
+NEAR_TIE = 1e-6   # a draw closer than this to a CDF boundary may differ between implementations
+
+
+# ----------------------------------------------------------------------------
+# Teams and the paged cache (reading R1)
+# ----------------------------------------------------------------------------
+
+def num_teams(L, T):
+    """Number of teams of a sequence of L tokens with team size T (R1)."""
+    return (int(L) + T - 1) // T
+
+
+def team_size(L, T, t):
+    """Valid tokens in team t of a sequence of L tokens (the last may be short, R1)."""
+    return min(T, int(L) - t * T)
+
+
+def team_tokens(pages_f64, page_table_row, L, T, g, t):
+    """Rows [n_t][d] of team t of one sequence, KV head g, from the paged cache.
+
+    Layout: pages[physical_page][kv_head][slot][d]; team t of the sequence is
+    logical page t, stored at physical page page_table_row[t] (R1).
+    """
+    n = team_size(L, T, t)
+    return pages_f64[int(page_table_row[t]), g, :n, :]
+
+
+# ----------------------------------------------------------------------------
+# Representatives (reading R2)
+# ----------------------------------------------------------------------------
+
+def build_reps(k_pages, page_table, seq_lens, page_size, dtype, pages=None):
+    """Mean key of every referenced team, rounded once to the KV type.
+
+    [EXP] section 三 step 2: one representative key per team (mean, medoid or
+    random are listed); [ABS]: the query scores one representative from each
+    team. Reading R2: the mean, as math.fsum(column) / n (exact sum, one
+    correctly rounded divide), then one round-to-nearest-even into the KV type.
+
+    Returns a float64 array [num_pages][Hkv][d]; pages no sequence references
+    (or not in ``pages`` when given) are NaN.
+    """
+    num_pages, hkv, T, d = k_pages.shape
+    reps = np.full((num_pages, hkv, d), np.nan)
+    want = None if pages is None else set(int(p) for p in pages)
+    for b in range(len(seq_lens)):
+        L = int(seq_lens[b])
+        for t in range(num_teams(L, T)):
+            p = int(page_table[b][t])
+            if want is not None and p not in want:
+                continue
+            n = team_size(L, T, t)
+            keys = decode(k_pages[p, :, :n, :], dtype)          # [Hkv][n][d]
+            for g in range(hkv):
+                for c in range(d):
+                    reps[p, g, c] = math.fsum(keys[g, :, c]) / n
+            reps[p] = round_to_dtype(reps[p], dtype)
+    return reps
+
+
+# ----------------------------------------------------------------------------
+# Selection: scores, team softmax, draws, inclusion probabilities
+# ----------------------------------------------------------------------------
+
+def rep_scores(q_h, rep_rows):
+    """s_t = (1/sqrt(d)) * q . rep_t for every team ([EXP] section 三 step 2; R3).
+
+    The products of two bfloat16 or two binary32 values are exact in float64;
+    math.fsum makes each dot product correctly rounded.
+    """
+    d = q_h.shape[0]
+    inv_sqrt_d = 1.0 / math.sqrt(d)
+    return np.array([math.fsum(q_h * r) * inv_sqrt_d for r in rep_rows])
+
+
+def team_softmax(s):
+    """Team-level softmax and its cumulative sums ([EXP] section 三 step 2).
+
+    Returns (e, C, Z, p): e_t = exp(s_t - max s); C_t = e_0 + ... + e_t summed
+    left to right; Z = C_last; p_t = e_t / Z.
+    """
+    m = max(s)
+    e = np.array([math.exp(x - m) for x in s])
+    C = np.empty_like(e)
+    acc = 0.0
+    for t, x in enumerate(e):
+        acc += x
+        C[t] = acc
+    Z = C[-1]
+    return e, C, Z, e / Z
+
+
+def inverse_cdf(u, e, C, Z):
+    """Team drawn by uniform u: the first t with u * Z < C_t.
+
+    Strict '<' on the unnormalised cumulative sums never selects a team with
+    zero mass. If rounding leaves no such t, the last team with positive mass
+    is taken (this cannot happen for u < 1, kept as a guard).
+    """
+    x = u * Z
+    for t in range(len(C)):
+        if x < C[t]:
+            return t
+    return int(np.nonzero(e > 0)[0][-1])
+
+
+def draw_distance_to_boundary(u, C, Z):
+    """Distance from u to the nearest interior CDF boundary C_t / Z (t < K-1)."""
+    if len(C) < 2:
+        return math.inf
+    return float(np.min(np.abs(u - C[:-1] / Z)))
+
+
+def inclusion_probability(p, M):
+    """pi = 1 - (1 - p)^M, computed as -expm1(M * log1p(-p)) (R4).
+
+    [ABS]: each sampled team is re-weighted by the inverse of its inclusion
+    probability; with M independent draws the chance that team t is drawn at
+    least once is 1 - (1 - p_t)^M.
+    """
+    return -math.expm1(M * math.log1p(-p))
+
+
+class Selection:
+    """Result of sampling teams for one query head."""
+
+    def __init__(self, teams, pi, p, near_tie_teams, draws, full):
+        self.teams = teams                  # ascending unique team indices
+        self.pi = pi                        # inclusion probability of each, same order
+        self.p = p                          # team probabilities, all teams
+        self.near_tie_teams = near_tie_teams  # teams reached or missed via a near-tie draw
+        self.draws = draws                  # raw draw results t_j (empty if full)
+        self.full = full                    # True when every team is read (R6)
+
+    @property
+    def inv_pi(self):
+        return [1.0 / x for x in self.pi]
+
+
+def select_teams(q_h, rep_rows, M, seed, offset, b, h):
+    """Sample teams for one query head (steps 2-3 of [EXP] section 三; [ABS]; R4, R6, R7).
+
+    Draw j uses uniform u_j from Philox4x32-10 (see oracle/philox.py for the
+    counter layout) and takes team inverse_cdf(u_j). Draws whose uniform lies
+    within NEAR_TIE of a CDF boundary are recorded: both neighbouring teams
+    are listed in near_tie_teams.
+    """
+    K = len(rep_rows)
+    s = rep_scores(q_h, rep_rows)
+    e, C, Z, p = team_softmax(s)
+    if M >= K:
+        teams = list(range(K))
+        return Selection(teams, [1.0] * K, p, set(), [], True)
+    near = set()
+    draws = []
+    for x in draw_words(M, seed, offset, b, h):
+        u = word_to_uniform(x)
+        t = inverse_cdf(u, e, C, Z)
+        draws.append(t)
+        if draw_distance_to_boundary(u, C, Z) < NEAR_TIE:
+            k = int(np.argmin(np.abs(u - C[:-1] / Z)))
+            near.update((k, k + 1))
+    teams = sorted(set(draws))
+    pi = [inclusion_probability(p[t], M) for t in teams]
+    return Selection(teams, pi, p, near, draws, False)
+
+
+# ----------------------------------------------------------------------------
+# Estimation inside the sampled teams
+# ----------------------------------------------------------------------------
+
+def token_scores(q_h, keys):
+    """s_j = (1/sqrt(d)) * q . k_j for the rows of ``keys`` (R3)."""
+    d = q_h.shape[0]
+    return (keys @ q_h) * (1.0 / math.sqrt(d))
+
+
+def ht_sums(q_h, team_kv, weights, shift):
+    """Re-weighted sums over the sampled teams ([EXP] steps 4-5; [ABS]; R5).
+
+    team_kv: list of (keys [n][d], values [n][d]) for the sampled teams;
+    weights: w_t for each (1/pi_t). Returns (numerator [d], denominator):
+      N = sum_t w_t sum_{j in t} exp(s_j - shift) v_j
+      D = sum_t w_t sum_{j in t} exp(s_j - shift)
+    """
+    d = q_h.shape[0]
+    num = np.zeros(d)
+    den = 0.0
+    for (keys, vals), w in zip(team_kv, weights):
+        a = np.exp(token_scores(q_h, keys) - shift)
+        num += w * (a @ vals)
+        den += w * a.sum()
+    return num, den
+
+
+def estimate(q_h, team_kv, weights):
+    """Estimated attention output and log-sum-exp from sampled teams (R5).
+
+    out = N / D; lse = shift + log(D), where shift is the largest token score
+    among the sampled teams (it cancels in out). An empty team list (an empty
+    sequence) gives out = 0 and lse = -inf (R8).
+    """
+    d = q_h.shape[0]
+    if not team_kv:
+        return np.zeros(d), -math.inf
+    shift = max(float(np.max(token_scores(q_h, k))) for k, _ in team_kv)
+    num, den = ht_sums(q_h, team_kv, weights, shift)
+    return num / den, shift + math.log(den)
+
+
+def dense_attention(q_h, keys, vals):
+    """Exact softmax attention of one query over all L cached tokens.
+
+    The dense baseline SANTA++ is compared against ([ABS]: the dense-attention
+    baseline). Returns (out [d], lse).
+    """
+    if keys.shape[0] == 0:
+        return np.zeros(q_h.shape[0]), -math.inf
+    s = token_scores(q_h, keys)
+    m = float(np.max(s))
+    a = np.exp(s - m)
+    return (a @ vals) / a.sum(), m + math.log(a.sum())
+
+
+# ----------------------------------------------------------------------------
+# Whole decode step over a paged batch
+# ----------------------------------------------------------------------------
+
+class PagedKV:
+    """Float64 view of a paged KV cache as the library lays it out.
+
+    k_pages, v_pages: stored arrays [num_pages][Hkv][T][d] (uint16 bf16 bits
+    or float32); page_table [B][max_pages]; seq_lens [B]. Pages are decoded to
+    float64 on first use.
+    """
+
+    def __init__(self, dtype, k_pages, v_pages, page_table, seq_lens):
+        self.dtype = dtype
+        self.k_raw, self.v_raw = k_pages, v_pages
+        self.page_table = np.asarray(page_table)
+        self.seq_lens = np.asarray(seq_lens)
+        self.num_pages, self.hkv, self.T, self.d = k_pages.shape
+        self._k, self._v = {}, {}
+
+    def _page(self, cache, raw, p):
+        if p not in cache:
+            cache[p] = decode(raw[p], self.dtype)
+        return cache[p]
+
+    def team(self, b, g, t):
+        """(keys [n][d], values [n][d]) of team t of sequence b, KV head g."""
+        L = int(self.seq_lens[b])
+        p = int(self.page_table[b][t])
+        n = team_size(L, self.T, t)
+        return (self._page(self._k, self.k_raw, p)[g, :n, :],
+                self._page(self._v, self.v_raw, p)[g, :n, :])
+
+    def all_tokens(self, b, g):
+        L = int(self.seq_lens[b])
+        K = num_teams(L, self.T)
+        if K == 0:
+            return np.zeros((0, self.d)), np.zeros((0, self.d))
+        parts = [self.team(b, g, t) for t in range(K)]
+        return np.concatenate([k for k, _ in parts]), np.concatenate([v for _, v in parts])
+
+
+class HeadResult:
+    def __init__(self, out, lse, selection):
+        self.out, self.lse, self.selection = out, lse, selection
+
+
+def santa_head(kv, q_h, reps, b, h, num_q_heads, M, seed, offset):
+    """SANTA++ for one (sequence b, query head h): select teams, then estimate.
+
+    q_h: float64 query [d]; reps: float64 [num_pages][Hkv][d] (from build_reps).
+    KV head of query head h is h // (Hq / Hkv) (grouped-query attention).
+    """
+    g = h // (num_q_heads // kv.hkv)
+    L = int(kv.seq_lens[b])
+    K = num_teams(L, kv.T)
+    if K == 0:
+        return HeadResult(np.zeros(kv.d), -math.inf, Selection([], [], np.zeros(0), set(), [], True))
+    rep_rows = np.stack([reps[int(kv.page_table[b][t]), g] for t in range(K)])
+    sel = select_teams(q_h, rep_rows, M, seed, offset, b, h)
+    out, lse = estimate(q_h, [kv.team(b, g, t) for t in sel.teams], sel.inv_pi)
+    return HeadResult(out, lse, sel)
+
+
+def evaluate_given_set(kv, q_h, b, h, num_q_heads, teams, inv_pi):
+    """Estimate for a supplied team set and weights (used when a near-tie draw
+    made the HIP path pick a different but equally valid set)."""
+    g = h // (num_q_heads // kv.hkv)
+    return estimate(q_h, [kv.team(b, g, t) for t in teams], list(inv_pi))
+
+
+def dense_head(kv, q_h, b, h, num_q_heads):
+    g = h // (num_q_heads // kv.hkv)
+    k, v = kv.all_tokens(b, g)
+    return dense_attention(q_h, k, v)
+
+
+# ----------------------------------------------------------------------------
+# Read accounting and closed forms
+# ----------------------------------------------------------------------------
+
+def expected_set_size(p, M):
+    """E|S| = sum_t pi_t for M draws with replacement (closed form of R4)."""
+    if M >= len(p):
+        return float(len(p))
+    return math.fsum(inclusion_probability(x, M) for x in p)
+
+
+def expected_union_size(p_heads, M):
+    """E|union over heads of S_h| = sum_t (1 - prod_h (1 - p_ht)^M), independent heads (R7)."""
+    K = len(p_heads[0])
+    if M >= K:
+        return float(K)
+    total = []
+    for t in range(K):
+        miss = 1.0
+        for p in p_heads:
+            miss *= math.exp(M * math.log1p(-p[t]))
+        total.append(1.0 - miss)
+    return math.fsum(total)

@@ -1,0 +1,355 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a published value, a library routine
+that is not the one the oracle calls, a closed form, an exact enumeration or
+an invariant, chosen so that a dropped term, a wrong sign, a wrong index or a
+transposed operand in the oracle fails at least one of them.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import numerics, philox, santa
+from sampled_sparse_decode_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# Philox4x32-10: published known-answer vectors
+# --------------------------------------------------------------------------
+
+def _kat_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            w = [int(x, 16) for x in line.split()]
+            rows.append((tuple(w[0:4]), tuple(w[4:6]), tuple(w[6:10])))
+    return rows
+
+
+@pytest.mark.parametrize("ctr,key,expected", _kat_rows())
+def test_philox_known_answers(ctr, key, expected):
+    assert philox.philox4x32_10(ctr, key) == expected
+
+
+def test_philox_draw_layout_streams_differ():
+    # Different heads, sequences and offsets read different counters.
+    a = philox.draw_words(8, 0, 0, 0, 0)
+    assert a != philox.draw_words(8, 0, 0, 0, 1)
+    assert a != philox.draw_words(8, 0, 0, 1, 0)
+    assert a != philox.draw_words(8, 0, 1, 0, 0)
+    assert a != philox.draw_words(8, 1, 0, 0, 0)
+    # Draw j is word j mod 4 of block j div 4.
+    blk = philox.philox4x32_10((1, 3, 2, 5), (7, 0))
+    assert philox.draw_words(8, 7, 5, 2, 3)[4:8] == list(blk)
+
+
+def test_uniform_mapping_open_interval():
+    assert philox.word_to_uniform(0) == 2.0 ** -33
+    assert philox.word_to_uniform(0xFFFFFFFF) == 1.0 - 2.0 ** -33
+
+
+# --------------------------------------------------------------------------
+# bfloat16 decode and rounding against torch's conversions
+# --------------------------------------------------------------------------
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=20000, dtype=np.uint16)
+    exp = (bits >> 7) & 0xFF
+    bits = bits[exp != 0xFF]                 # no inf / nan
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(numerics.decode_bf16(bits), ref)
+
+
+def test_bf16_round_matches_torch_on_binary32_values():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),     # binary32 subnormals
+        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)], dtype=np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = numerics.round_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_round_is_one_step():
+    # 1 + 2^-8 + 2^-40 is above the tie between 1 and 1 + 2^-7, so it rounds up;
+    # rounding first to binary32 would land on the tie and go down to 1.
+    assert numerics.round_to_bf16(1.0 + 2 ** -8 + 2 ** -40) == 1.0 + 2 ** -7
+    assert numerics.round_to_bf16(1.0 + 2 ** -8) == 1.0                  # tie -> even
+    assert numerics.round_to_bf16(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6     # tie -> even
+    assert numerics.round_to_bf16(2.0 ** 128) == math.inf
+    big = float.fromhex("0x1.fep127")
+    assert numerics.round_to_bf16(big) == big
+
+
+def _fraction_round_bf16(fr):
+    """Independent exact rounding of a rational to bfloat16 (normal range)."""
+    if fr == 0:
+        return 0.0
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    scaled = a * 128                      # 8 significant bits
+    r = round(scaled)                     # Python rounds Fractions half to even
+    return sign * float(Fraction(r, 128) * Fraction(2) ** e)
+
+
+def test_reps_are_exact_rounded_means():
+    rng = np.random.default_rng(2)
+    T, d = 8, 16
+    lens = [8 * 3 + 3]                    # a ragged last team of 3 tokens
+    keys = rng.standard_normal((1, 1, lens[0], d)).astype(np.float32)
+    w = wl._contiguous("t", "bf16", keys, keys, np.zeros((1, 1, d), np.float32), T, 4)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, T, "bf16")
+    kd = numerics.decode_bf16(w.k_pages)
+    for t in range(4):
+        n = santa.team_size(lens[0], T, t)
+        for c in range(d):
+            exact = sum(Fraction(float(v)) for v in kd[t, 0, :n, c]) / n
+            assert reps[t, 0, c] == _fraction_round_bf16(exact)
+
+
+# --------------------------------------------------------------------------
+# Dense attention and team scores against torch's attention routine
+# --------------------------------------------------------------------------
+
+def test_dense_matches_torch_sdpa():
+    rng = np.random.default_rng(3)
+    for L, d in [(1, 8), (37, 64), (300, 128)]:
+        q = rng.standard_normal(d)
+        k = rng.standard_normal((L, d)) * 2
+        v = rng.standard_normal((L, d))
+        out, _ = santa.dense_attention(q, k, v)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, None, None], torch.from_numpy(k)[None, None],
+            torch.from_numpy(v)[None, None])[0, 0, 0].numpy()
+        assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_dense_lse_matches_torch_logsumexp():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal(32)
+    k = rng.standard_normal((50, 32)) * 3
+    _, lse = santa.dense_attention(q, k, k)
+    ref = torch.logsumexp(torch.from_numpy(k) @ torch.from_numpy(q) / math.sqrt(32), 0).item()
+    assert abs(lse - ref) < 1e-12
+
+
+def test_one_token_teams_give_attention_weights():
+    # With one token per team the representative is the key itself, so the
+    # team probabilities are the attention weights of the dense softmax.
+    rng = np.random.default_rng(5)
+    L, d = 40, 16
+    keys = rng.standard_normal((1, 1, L, d)).astype(np.float32)
+    q = rng.standard_normal((1, 1, d)).astype(np.float32)
+    w = wl._contiguous("t", "f32", keys, keys, q, 1, 4)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, 1, "f32")
+    qh = q[0, 0].astype(np.float64)
+    s = santa.rep_scores(qh, np.stack([reps[t, 0] for t in range(L)]))
+    _, _, _, p = santa.team_softmax(s)
+    eye = torch.eye(L, dtype=torch.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qh)[None, None, None], torch.from_numpy(keys[0, 0].astype(np.float64))[None, None],
+        eye[None, None])[0, 0, 0].numpy()
+    assert np.max(np.abs(p - ref)) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Whole-pipeline special cases
+# --------------------------------------------------------------------------
+
+def _kv(w):
+    return santa.PagedKV(w.dtype, w.k_pages, w.v_pages, w.page_table, w.seq_lens)
+
+
+def test_full_coverage_equals_dense():
+    w = wl.tiny_planted(n=200, d=32, T=16, M=13)    # 13 teams, M >= K
+    kv = _kv(w)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    qh = numerics.decode(w.q[0, 0], w.dtype)
+    r = santa.santa_head(kv, qh, reps, 0, 0, 1, w.M, 0, 0)
+    assert r.selection.full and r.selection.teams == list(range(13))
+    out, lse = santa.dense_head(kv, qh, 0, 0, 1)
+    assert np.max(np.abs(r.out - out)) < 1e-12 and abs(r.lse - lse) < 1e-12
+
+
+def test_constant_values_give_constant_output():
+    w = wl.qwen_planted(batch=1, seq_len=1000, T=64, hq=4, hkv=2, d=64, plants=2, M=5, dtype="bf16")
+    w.v_pages[:] = numerics.bf16_bits_of(np.array([1.5]))[0]
+    kv = _kv(w)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    for h in range(4):
+        r = santa.santa_head(kv, numerics.decode(w.q[0, h], "bf16"), reps, 0, h, 4, w.M, 7, 3)
+        assert np.max(np.abs(r.out - 1.5)) < 1e-12
+
+
+def test_permuted_page_table_same_result():
+    w = wl.paged_ragged(num_seqs=3, len_min=500, len_max=2000, T=64, M=6, hq=4, hkv=2, d=64)
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(w.num_pages)            # new physical position of each page
+    k2 = np.empty_like(w.k_pages)
+    v2 = np.empty_like(w.v_pages)
+    k2[perm] = w.k_pages
+    v2[perm] = w.v_pages
+    pt2 = perm[w.page_table].astype(np.int32)
+    kv1, kv2 = _kv(w), santa.PagedKV(w.dtype, k2, v2, pt2, w.seq_lens)
+    r1 = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    r2 = santa.build_reps(k2, pt2, w.seq_lens, w.page_size, w.dtype)
+    for b in range(3):
+        for h in range(4):
+            qh = numerics.decode(w.q[b, h], w.dtype)
+            a = santa.santa_head(kv1, qh, r1, b, h, 4, w.M, 1, 0)
+            c = santa.santa_head(kv2, qh, r2, b, h, 4, w.M, 1, 0)
+            assert a.selection.teams == c.selection.teams
+            assert np.array_equal(a.out, c.out) and a.lse == c.lse
+
+
+def test_empty_sequence():
+    w = wl.paged_ragged(num_seqs=2, len_min=100, len_max=300, T=32, M=4, hq=2, hkv=1, d=64)
+    w.seq_lens[1] = 0
+    kv = _kv(w)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    r = santa.santa_head(kv, numerics.decode(w.q[1, 0], w.dtype), reps, 1, 0, 2, w.M, 0, 0)
+    assert r.lse == -math.inf and np.all(r.out == 0)
+
+
+# --------------------------------------------------------------------------
+# Inverse CDF
+# --------------------------------------------------------------------------
+
+def test_inverse_cdf_uniform_mass_closed_form():
+    K = 10
+    e = np.ones(K)
+    C = np.cumsum(e)
+    for x in range(1, 1000):
+        u = x / 1000 + 1e-7
+        assert santa.inverse_cdf(u, e, C, C[-1]) == int(math.floor(u * K))
+
+
+def test_inverse_cdf_never_picks_zero_mass():
+    e = np.array([0.0, 1.0, 0.0, 0.0, 2.0, 0.0])
+    C = np.cumsum(e)
+    for u in np.linspace(1e-9, 1 - 1e-9, 997):
+        assert santa.inverse_cdf(u, e, C, C[-1]) in (1, 4)
+
+
+def test_draw_frequencies_chi_square():
+    from scipy.stats import chisquare
+    rng = np.random.default_rng(11)
+    s = rng.standard_normal(24)
+    e, C, Z, p = santa.team_softmax(s)
+    counts = np.zeros(24)
+    for seed in range(300):
+        for x in philox.draw_words(64, seed, 0, 0, 0):
+            counts[santa.inverse_cdf(philox.word_to_uniform(x), e, C, Z)] += 1
+    assert chisquare(counts, p * counts.sum()).pvalue > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Horvitz-Thompson sums: exact enumeration on tiny inputs
+# --------------------------------------------------------------------------
+
+def _tiny_five_teams(seed):
+    rng = np.random.default_rng(seed)
+    d, T, L = 8, 4, 19                       # teams of 4,4,4,4,3 tokens
+    keys = (rng.standard_normal((1, 1, L, d)) * 1.5).astype(np.float32)
+    vals = rng.standard_normal((1, 1, L, d)).astype(np.float32)
+    q = rng.standard_normal((1, 1, d)).astype(np.float32)
+    return wl._contiguous("five", "f32", keys, vals, q, T, 1)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_ht_sums_unbiased_by_enumeration(M):
+    w = _tiny_five_teams(12 + M)
+    kv = _kv(w)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    qh = numerics.decode(w.q[0, 0], "f32")
+    K = 5
+    s = santa.rep_scores(qh, np.stack([reps[t, 0] for t in range(K)]))
+    _, _, _, p = santa.team_softmax(s)
+    teams = [kv.team(0, 0, t) for t in range(K)]
+    keys, vals = kv.all_tokens(0, 0)
+    a = np.exp(santa.token_scores(qh, keys))
+    N_exact, D_exact = a @ vals, a.sum()
+    EN, ED = np.zeros(w.head_dim), 0.0
+    incl = np.zeros(K)
+    for seq in itertools.product(range(K), repeat=M):
+        prob = float(np.prod([p[t] for t in seq]))
+        S = sorted(set(seq))
+        wts = [1.0 / santa.inclusion_probability(p[t], M) for t in S]
+        n, dd = santa.ht_sums(qh, [teams[t] for t in S], wts, 0.0)
+        EN += prob * n
+        ED += prob * dd
+        for t in S:
+            incl[t] += prob
+    assert abs(ED - D_exact) < 1e-12 * abs(D_exact)
+    assert np.max(np.abs(EN - N_exact)) < 1e-12 * np.max(np.abs(N_exact))
+    for t in range(K):
+        assert abs(incl[t] - santa.inclusion_probability(p[t], M)) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Monte Carlo over Philox seeds: convergence and closed-form set size
+# --------------------------------------------------------------------------
+
+def test_monte_carlo_converges_and_set_size_closed_form():
+    w = wl.tiny_planted(n=512, d=32, T=32, M=6)
+    kv = _kv(w)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    qh = numerics.decode(w.q[0, 0], "f32")
+    keys, vals = kv.all_tokens(0, 0)
+    out_d, lse_d = santa.dense_attention(qh, keys, vals)
+    R = 3000
+    Dr = np.empty(R)
+    Nr = np.empty((R, w.head_dim))
+    sizes = np.empty(R)
+    for seed in range(R):
+        r = santa.santa_head(kv, qh, reps, 0, 0, 1, w.M, seed, 0)
+        Dr[seed] = math.exp(r.lse - lse_d)           # estimated D / exact D
+        Nr[seed] = r.out * Dr[seed]                  # estimated N / exact D
+        sizes[seed] = len(r.selection.teams)
+    se = Dr.std() / math.sqrt(R)
+    assert abs(Dr.mean() - 1.0) < 5 * se + 1e-12
+    seN = Nr.std(axis=0) / math.sqrt(R)
+    assert np.all(np.abs(Nr.mean(axis=0) - out_d) < 5 * seN + 1e-12)
+    # The ratio of the means converges to the dense output.
+    assert np.max(np.abs(Nr.mean(axis=0) / Dr.mean() - out_d)) < 10 * np.max(seN) / Dr.mean()
+    # Expected number of distinct teams: sum of inclusion probabilities.
+    K = santa.num_teams(int(w.seq_lens[0]), w.page_size)
+    s = santa.rep_scores(qh, np.stack([reps[t, 0] for t in range(K)]))
+    _, _, _, p = santa.team_softmax(s)
+    assert abs(sizes.mean() - santa.expected_set_size(p, w.M)) < 5 * sizes.std() / math.sqrt(R)
+
+
+def test_union_size_closed_form():
+    rng = np.random.default_rng(21)
+    K, M, G = 40, 5, 3
+    ps = [santa.team_softmax(rng.standard_normal(K))[3] for _ in range(G)]
+    R = 4000
+    sizes = np.empty(R)
+    for r in range(R):
+        u = set()
+        for h in range(G):
+            e, C, Z = ps[h], np.cumsum(ps[h]), np.cumsum(ps[h])[-1]
+            for x in philox.draw_words(M, r, 0, 0, h):
+                u.add(santa.inverse_cdf(philox.word_to_uniform(x), e, C, Z))
+        sizes[r] = len(u)
+    assert abs(sizes.mean() - santa.expected_union_size(ps, M)) < 5 * sizes.std() / math.sqrt(R)
