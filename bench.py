@@ -1,0 +1,220 @@
+"""Benchmark of SANTA++ decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers R]
+
+A step is one SANTA++ decode-attention call (representative scoring, team
+softmax, draws, inclusion probabilities, split-K gather, combine) for one
+layer of the workload. The workload is the Qwen2.5-7B-shaped 32K-context
+layer with M = 31 by default. Its cache is replicated R times ("layers",
+about 1 GiB in total) and the steps cycle through them, so every step reads
+HBM rather than the 256 MB last-level cache, as a real decode step does when
+it moves from one layer's cache to the next. Inputs are resident in HBM
+before timing starts. The same is timed for the dense decode kernel, and for
+the gather + combine stage alone (the kernel that moves the bytes), whose
+algorithmic bytes give the roofline figure. The CPU oracle is timed on a
+bounded sample of the same workload at the end.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, AMD public specification
+LLC_BYTES = 256 << 20         # MI355X Infinity Cache
+
+METRIC = "decode-attn µs/layer + HBM GB/s (% peak), 32K ctx M=31, vs own dense decode"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="qwen7b_32k_b1_m31")
+    ap.add_argument("--layers", type=int, default=0, help="cache copies to cycle through (0 = enough for 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def union_stats(w, sampled):
+    """Per (b, g) union of the query heads' drawn teams, from the returned sets."""
+    G = w.group
+    T = w.page_size
+    stats = []
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        K = (L + T - 1) // T
+        for g in range(w.num_kv_heads):
+            u = set()
+            per_head = []
+            for h in range(g * G, (g + 1) * G):
+                s = [int(t) for t in sampled[b, h] if t >= 0]
+                per_head.append(s)
+                u.update(s)
+            stats.append((b, g, L, K, sorted(u), per_head))
+    return stats
+
+
+def team_tokens(L, T, t):
+    return min(T, L - t * T)
+
+
+def algorithmic_bytes(w, stats):
+    """Bytes the hot path must move, by the definition in the design notes.
+
+    attend (gather + combine): K and V of every union team once per (b, g),
+    the G queries, and out + lse. select: every representative once per
+    (b, g) plus the queries. dense: K and V of every token, queries, out + lse.
+    """
+    e, d, G, T = w.elem_bytes, w.head_dim, w.group, w.page_size
+    attend = select = dense = 0
+    head_reads = dense_head_reads = 0
+    for b, g, L, K, u, per_head in stats:
+        kv_union = sum(2 * team_tokens(L, T, t) * d * e for t in u)
+        io = G * d * e + G * (d + 1) * 4
+        attend += kv_union + io
+        select += K * d * e + G * d * e
+        dense += 2 * L * d * e + io
+        for s in per_head:
+            head_reads += K * d * e + sum(2 * team_tokens(L, T, t) * d * e for t in s)
+            dense_head_reads += 2 * L * d * e
+    return dict(attend=attend, select=select, step=attend + select, dense=dense,
+                frac_head=head_reads / dense_head_reads, frac_hbm=(attend + select) / dense)
+
+
+def time_loop(fn, steps, warmup, torch):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps       # microseconds per call
+
+
+def cpu_baseline(w, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same step."""
+    from oracle import numerics, santa as osanta
+    kv = osanta.PagedKV(w.dtype, w.k_pages, w.v_pages, w.page_table, w.seq_lens)
+    heads = [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
+    pages = set()
+    for b in range(w.batch):
+        K = osanta.num_teams(int(w.seq_lens[b]), w.page_size)
+        pages.update(int(x) for x in w.page_table[b][:K])
+    reps = osanta.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype, pages=pages)
+    qs = {bh: numerics.decode(w.q[bh], w.dtype) for bh in heads}
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < len(heads) * 4:
+        b, h = heads[done % len(heads)]
+        osanta.santa_head(kv, qs[(b, h)], reps, b, h, w.num_q_heads, w.M, w.seed, done // len(heads))
+        done += 1
+    el = time.perf_counter() - t0
+    us_per_layer = el / done * len(heads) * 1e6
+    return {"value": round(us_per_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (sequence, query head) SANTA++ evaluations of {w.name} "
+                      f"({len(heads)} per layer), single-threaded float64 Python/numpy oracle, "
+                      f"representatives precomputed; scaled to one layer"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a "
+              f"design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sampled_sparse_decode_amd import santa as S, workloads as W
+
+    w = W.FULL_SIZE[args.workload]()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kv0, q = S.kv_from_workload(w, dev)
+    kv_bytes = 2 * kv0.k_pages.numel() * kv0.k_pages.element_size()
+    R = args.layers or max(4, math.ceil(4 * LLC_BYTES / kv_bytes))
+    layers = [kv0]
+    for _ in range(R - 1):
+        layers.append(S.KVCache(kv0.k_pages.clone(), kv0.v_pages.clone(), kv0.page_table, kv0.seq_lens,
+                                w.num_q_heads))
+    reps = [S.santa_build_reps(kv) for kv in layers]
+    M = w.M
+    wss = [S.make_workspace(kv, M) for kv in layers]
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    # Sets of this step (identical on every layer copy) for the byte count.
+    _, _, sampled, _ = S.santa_decode_attention(kv0, q, reps[0], M, w.seed, w.offset, wss[0], return_sets=True)
+    torch.cuda.synchronize()
+    stats = union_stats(w, sampled.cpu().numpy())
+    ab = algorithmic_bytes(w, stats)
+
+    def santa_step(i):
+        j = i % R
+        S.santa_decode_attention(layers[j], q, reps[j], M, w.seed, w.offset, wss[j], out, lse)
+
+    def dense_step(i):
+        j = i % R
+        S.dense_decode_attention(layers[j], q, wss[j], out, lse)
+
+    def attend_step(i):
+        j = i % R
+        S.santa_attend_selected(layers[j], q, M, wss[j], out, lse)
+
+    santa_us = time_loop(santa_step, args.steps, args.warmup, torch)
+    dense_us = time_loop(dense_step, args.steps, args.warmup, torch)
+    for j in range(R):
+        S.santa_select_teams(layers[j], q, reps[j], M, w.seed, w.offset, wss[j])
+    attend_us = time_loop(attend_step, args.steps, args.warmup, torch)
+
+    attend_gbps = ab["attend"] / (attend_us * 1e-6) / 1e9
+    step_gbps = ab["step"] / (santa_us * 1e-6) / 1e9
+    dense_gbps = ab["dense"] / (dense_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(santa_us, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(santa_us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": int(w.seq_lens.max()),
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "team_size": w.page_size, "M": M, "layers_cycled": R},
+        "santa": {"us_per_layer": round(santa_us, 3), "hbm_gbps": round(step_gbps, 1),
+                  "pct_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2), "bytes": ab["step"]},
+        "dense": {"us_per_layer": round(dense_us, 3), "hbm_gbps": round(dense_gbps, 1),
+                  "pct_peak": round(100 * dense_gbps / HBM_PEAK_GBPS, 2), "bytes": ab["dense"]},
+        "speedup_vs_dense": round(dense_us / santa_us, 3),
+        "kv_read_fraction": {"per_query_head": round(ab["frac_head"], 4), "hbm": round(ab["frac_hbm"], 4)},
+        "roofline": {"kernel": "gather+combine (santa_attend_selected)", "bound": "hbm",
+                     "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attend_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "us_per_launch": round(attend_us, 3), "bytes_per_launch": ab["attend"]},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

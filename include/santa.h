@@ -1,0 +1,192 @@
+/*
+ * libsanta — SANTA++ sampled-team decode attention for AMD MI355X (gfx950).
+ *
+ * Sources (cited by title and section):
+ *   [ABS] "SANTA++: Sampling Attention through Representative Keys",
+ *         arXiv 2609.35629, abstract.
+ *   [EXP] "SANTA++：用代表性 Key 采样把 KV cache 读带宽砍掉 80%" (explainer),
+ *         section 三 (core method) and its sub-sections 3.1-3.2.
+ *
+ * What the library computes, for one decode step of one attention layer
+ * ([ABS]; [EXP] section 三): every new query (one per sequence and query head)
+ * scores one representative key per team of cached tokens, turns the scores
+ * into a team-level softmax p, draws M teams from p, computes exact attention
+ * only inside the drawn teams, and weights each drawn team by the inverse of
+ * its inclusion probability pi = 1 - (1 - p)^M, which makes the result an
+ * estimate of attention over the whole cache. A dense decode over every
+ * cached token, built from the same kernels, is exported as the baseline.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every array argument is a device (HBM) pointer, owned by the
+ *           caller, 16-byte aligned, densely packed in the layout stated.
+ *           The library allocates nothing and keeps no state between calls;
+ *           calls are re-entrant and may run concurrently on different
+ *           streams if their output and workspace buffers differ.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *           stream). All work is enqueued on it and the call returns before
+ *           it runs; buffers must stay valid until the stream reaches it.
+ * Errors.   Arguments are checked on the host before any HIP call; a bad
+ *           argument returns a status and enqueues nothing. A launch failure
+ *           returns SANTA_ERR_HIP. Values that live in device memory
+ *           (seq_lens, page_table, teams) are not visible to the host: the
+ *           kernels clamp sequence lengths to [0, page_size * max_pages_per_seq]
+ *           and page ids to [0, num_pages - 1] so they never read out of
+ *           bounds, but results for such inputs are meaningless.
+ * Results.  Deterministic: the same inputs, seed and offset give bitwise
+ *           identical outputs (no floating-point atomics; partial results
+ *           are merged in a fixed order).
+ *
+ * Paged KV layout (all entry points)
+ * ----------------------------------
+ *   k_pages, v_pages  [num_pages][num_kv_heads][page_size][head_dim], dtype
+ *   page_table        [batch][max_pages_per_seq] int32: physical page of
+ *                     logical team t of sequence b
+ *   seq_lens          [batch] int32: cached tokens L_b of sequence b
+ * A team is one page: team t of sequence b is tokens [t*T, min((t+1)*T, L_b))
+ * stored in physical page page_table[b][t] (T = page_size). The pages leave
+ * the team partition open ([EXP] 3.2); contiguous runs, one per page, is
+ * this library's choice. Sequence b has K_b = ceil(L_b / T) teams.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef SANTA_H
+#define SANTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum santa_status {
+    SANTA_OK = 0,
+    SANTA_ERR_NULL = 1,         /* a required pointer is NULL                      */
+    SANTA_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes              */
+    SANTA_ERR_UNSUPPORTED = 3,  /* valid but not built (dtype, head_dim, page_size) */
+    SANTA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required          */
+    SANTA_ERR_HIP = 5           /* a HIP launch failed                              */
+} santa_status;
+
+typedef enum santa_dtype {
+    SANTA_F32 = 0,              /* IEEE binary32                                    */
+    SANTA_BF16 = 1              /* bfloat16 (top 16 bits of a binary32)             */
+} santa_dtype;
+
+/* Supported sizes: dtype in {SANTA_F32, SANTA_BF16}; head_dim in {64, 128};
+ * page_size in {16, 32, 64, 128, 256}; num_q_heads % num_kv_heads == 0 with
+ * num_q_heads / num_kv_heads <= 16; 1 <= max_pages_per_seq <= 2048;
+ * 1 <= batch <= 65535; num_pages >= 1. */
+typedef struct santa_kv {
+    int32_t dtype;              /* santa_dtype of k_pages, v_pages, q and reps       */
+    int32_t batch;              /* B                                                 */
+    int32_t num_q_heads;        /* Hq                                                */
+    int32_t num_kv_heads;       /* Hkv                                               */
+    int32_t head_dim;           /* d                                                 */
+    int32_t page_size;          /* T: tokens per page = tokens per team              */
+    int32_t max_pages_per_seq;  /* row length of page_table                          */
+    int32_t reserved;           /* must be 0                                         */
+    int64_t num_pages;          /* physical pages in k_pages / v_pages               */
+    const void *k_pages;        /* [num_pages][Hkv][T][d] dtype                      */
+    const void *v_pages;        /* [num_pages][Hkv][T][d] dtype                      */
+    const int32_t *page_table;  /* [B][max_pages_per_seq]                            */
+    const int32_t *seq_lens;    /* [B], each in [0, T * max_pages_per_seq]           */
+} santa_kv;
+
+/* Bytes of device workspace that santa_decode_attention,
+ * santa_attention_given_teams and dense_decode_attention need for this cache
+ * shape. The workspace holds per-head team bitmaps and weights and the
+ * split-K partial results; its contents need no initialisation and are
+ * meaningless after the call. Returns SANTA_OK and writes *bytes, or a
+ * validation status. */
+santa_status santa_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes);
+
+/* Representative keys: reps[p][g][:] = the mean of the keys of team p for KV
+ * head g, rounded once (to nearest, ties to even) to the cache dtype.
+ * [EXP] section 三 step 2 (one representative key per team: mean, medoid or
+ * random are listed; the mean is used); [ABS] (the query scores one
+ * representative from each team). The mean is the float64 sum of the n valid
+ * keys divided by n (n < T only for a sequence's last team).
+ *   reps  [num_pages][Hkv][d] dtype, written for every page some sequence
+ *         references (team t < K_b); other pages are left untouched.
+ * Run once after prefill and again after a page's keys change. */
+santa_status santa_build_reps(const santa_kv *kv, void *reps, void *stream);
+
+/* SANTA++ decode attention ([ABS]; [EXP] section 三 steps 2-7).
+ * For each sequence b and query head h (KV head g):
+ *   1. s_t = q . reps[page(b,t)][g] / sqrt(d), summed in float64;
+ *   2. p = softmax(s) over the K_b teams, with cumulative sums C;
+ *   3. M draws with replacement by inverse CDF: draw j takes word j mod 4 of
+ *      Philox4x32-10 (Salmon et al., SC'11) with counter
+ *      (j / 4, h, b, offset) and key (seed & 0xffffffff, seed >> 32), maps it
+ *      to u = (word + 1/2) 2^-32 and picks the first t with u * C_last < C_t;
+ *      duplicates are removed. If M >= K_b every team is taken with pi = 1;
+ *   4. pi_t = 1 - (1 - p_t)^M, weight w_t = 1 / pi_t ([ABS]: inverse of the
+ *      inclusion probability);
+ *   5. exact scores q . k_j / sqrt(d) for the tokens of the drawn teams and
+ *      out = (sum_t w_t sum_j e^{s_j} v_j) / (sum_t w_t sum_j e^{s_j}),
+ *      lse = log(sum_t w_t sum_j e^{s_j}).
+ * Draws are independent per query head; the K/V tiles of a KV head are read
+ * once for the union of its query heads' drawn teams.
+ *   q        [B][Hq][d] dtype
+ *   reps     [num_pages][Hkv][d] dtype (from santa_build_reps)
+ *   M        draws per query head, >= 1
+ *   seed     Philox key; offset: Philox counter word 3 (advance it per
+ *            decode step and layer so every step draws afresh)
+ *   out      [B][Hq][d] float32
+ *   lse      [B][Hq] float32, or NULL
+ *   sampled  [B][Hq][M] int32 drawn team indices ascending, -1 padded, or NULL
+ *   inv_pi   [B][Hq][M] float32 weights 1/pi of `sampled` (0 padded), or NULL
+ * An empty sequence gives out = 0 and lse = -inf. */
+santa_status santa_decode_attention(const santa_kv *kv, const void *q, const void *reps,
+                                    int32_t M, uint64_t seed, uint32_t offset,
+                                    float *out, float *lse, int32_t *sampled, float *inv_pi,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* The two stages of santa_decode_attention, for callers that time or
+ * schedule them separately; running santa_select_teams and then
+ * santa_attend_selected on the same workspace equals one
+ * santa_decode_attention call.
+ *   santa_select_teams:    steps 1-4; writes the per-head team bitmaps and
+ *                          log-weights into `workspace` (and `sampled`,
+ *                          `inv_pi` when not NULL, as above).
+ *   santa_attend_selected: step 5 over the teams the last
+ *                          santa_select_teams call with this workspace and
+ *                          the same kv, M left in it; writes out and lse. */
+santa_status santa_select_teams(const santa_kv *kv, const void *q, const void *reps,
+                                int32_t M, uint64_t seed, uint32_t offset,
+                                int32_t *sampled, float *inv_pi,
+                                void *workspace, size_t workspace_bytes, void *stream);
+santa_status santa_attend_selected(const santa_kv *kv, const void *q, int32_t M,
+                                   float *out, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Dense decode attention over every cached token: the baseline SANTA++ is
+ * compared with ([ABS]: the dense attention baseline). Same kernels as step 5
+ * above with every team taken and w = 1.
+ *   q [B][Hq][d] dtype; out [B][Hq][d] float32; lse [B][Hq] float32 or NULL. */
+santa_status dense_decode_attention(const santa_kv *kv, const void *q, float *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step 5 alone, over caller-chosen teams and weights (for testing the
+ * estimator, or for a caller that samples teams itself).
+ *   teams   [B][Hq][M] int32 team indices of each head, -1 for unused slots;
+ *           indices outside [0, K_b) are ignored, repeats count once
+ *   weights [B][Hq][M] float32 w > 0 for each listed team
+ *   out, lse as in santa_decode_attention. */
+santa_status santa_attention_given_teams(const santa_kv *kv, const void *q, int32_t M,
+                                         const int32_t *teams, const float *weights,
+                                         float *out, float *lse,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *santa_status_string(int32_t status);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t santa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANTA_H */

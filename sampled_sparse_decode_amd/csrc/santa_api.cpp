@@ -1,0 +1,227 @@
+// C-ABI entry points of libsanta: argument validation, workspace carve-up,
+// split sizing and the launch sequence of each operation. Validation runs
+// before any HIP call so that bad arguments return a status without touching
+// the device.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "santa_internal.h"
+
+namespace santa {
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+santa_status validate_kv(const santa_kv *kv) {
+    if (!kv) return SANTA_ERR_NULL;
+    if (kv->dtype != SANTA_F32 && kv->dtype != SANTA_BF16) return SANTA_ERR_UNSUPPORTED;
+    if (kv->batch < 1 || kv->batch > 65535) return SANTA_ERR_SHAPE;
+    if (kv->num_q_heads < 1 || kv->num_kv_heads < 1) return SANTA_ERR_SHAPE;
+    if (kv->num_q_heads % kv->num_kv_heads != 0) return SANTA_ERR_SHAPE;
+    if (kv->num_q_heads / kv->num_kv_heads > kMaxGroup) return SANTA_ERR_UNSUPPORTED;
+    if (kv->head_dim != 64 && kv->head_dim != 128) return SANTA_ERR_UNSUPPORTED;
+    const int T = kv->page_size;
+    if (T != 16 && T != 32 && T != 64 && T != 128 && T != 256) return SANTA_ERR_UNSUPPORTED;
+    if (kv->max_pages_per_seq < 1 || kv->max_pages_per_seq > kMaxTeams) return SANTA_ERR_SHAPE;
+    if (kv->reserved != 0) return SANTA_ERR_SHAPE;
+    if (kv->num_pages < 1) return SANTA_ERR_SHAPE;
+    if (!kv->k_pages || !kv->v_pages || !kv->page_table || !kv->seq_lens) return SANTA_ERR_NULL;
+    return SANTA_OK;
+}
+
+WorkspaceLayout workspace_layout(const santa_kv &kv) {
+    WorkspaceLayout w{};
+    const size_t B = kv.batch, Hq = kv.num_q_heads, P = kv.max_pages_per_seq, d = kv.head_dim;
+    w.words = (kv.max_pages_per_seq + 31) / 32;
+    w.max_splits = kv.max_pages_per_seq;
+    size_t off = 0;
+    w.bitmaps = off;  off = align256(off + B * Hq * size_t(w.words) * 4);
+    w.lnw = off;      off = align256(off + B * Hq * P * 4);
+    w.part_ml = off;  off = align256(off + B * Hq * P * 8);
+    w.part_acc = off; off = align256(off + B * Hq * P * d * 4);
+    w.total = off;
+    return w;
+}
+
+// Union teams per split-K block: enough blocks to give every compute unit
+// several, few enough that the partial results stay a small share of the
+// bytes read.
+static int32_t teams_per_split(int64_t total_teams) {
+    int64_t tps = total_teams / 2048;
+    if (tps < 1) tps = 1;
+    if (tps > kMaxTeamsPerSplit) tps = kMaxTeamsPerSplit;
+    return int32_t(tps);
+}
+
+static Params base_params(const santa_kv &kv, const void *q, float *out, float *lse,
+                          void *workspace) {
+    Params p{};
+    const WorkspaceLayout w = workspace_layout(kv);
+    p.dtype = kv.dtype;
+    p.k_pages = kv.k_pages;
+    p.v_pages = kv.v_pages;
+    p.q = q;
+    p.page_table = kv.page_table;
+    p.seq_lens = kv.seq_lens;
+    p.num_pages = kv.num_pages;
+    p.B = kv.batch;
+    p.Hq = kv.num_q_heads;
+    p.Hkv = kv.num_kv_heads;
+    p.G = kv.num_q_heads / kv.num_kv_heads;
+    p.d = kv.head_dim;
+    p.T = kv.page_size;
+    p.P = kv.max_pages_per_seq;
+    p.words = w.words;
+    p.scale = 1.0 / std::sqrt(double(kv.head_dim));
+    char *ws = static_cast<char *>(workspace);
+    if (ws) {
+        p.bitmaps = reinterpret_cast<uint32_t *>(ws + w.bitmaps);
+        p.lnw = reinterpret_cast<float *>(ws + w.lnw);
+        p.part_ml = reinterpret_cast<float *>(ws + w.part_ml);
+        p.part_acc = reinterpret_cast<float *>(ws + w.part_acc);
+    }
+    p.out = out;
+    p.lse = lse;
+    return p;
+}
+
+static santa_status check_workspace(const santa_kv &kv, void *workspace, size_t bytes) {
+    if (!workspace) return SANTA_ERR_WORKSPACE;
+    if (bytes < workspace_layout(kv).total) return SANTA_ERR_WORKSPACE;
+    return SANTA_OK;
+}
+
+// Split-K gather then the cross-split combine, shared by all three attention
+// entry points once the per-head team bitmaps and weights are in place.
+static santa_status run_gather_combine(Params &p, void *stream) {
+    santa_status st = launch_gather(p, stream);
+    if (st != SANTA_OK) return st;
+    return launch_combine(p, stream);
+}
+
+}  // namespace santa
+
+using namespace santa;
+
+extern "C" {
+
+santa_status santa_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!bytes) return SANTA_ERR_NULL;
+    if (M < 1) return SANTA_ERR_SHAPE;
+    *bytes = workspace_layout(*kv).total;
+    return SANTA_OK;
+}
+
+santa_status santa_build_reps(const santa_kv *kv, void *reps, void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!reps) return SANTA_ERR_NULL;
+    Params p = base_params(*kv, nullptr, nullptr, nullptr, nullptr);
+    p.reps_out = reps;
+    return launch_build_reps(p, stream);
+}
+
+static santa_status santa_params(const santa_kv *kv, const void *q, int32_t M, float *out, float *lse,
+                                 void *workspace, size_t workspace_bytes, Params *p) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!q) return SANTA_ERR_NULL;
+    if (M < 1) return SANTA_ERR_SHAPE;
+    st = check_workspace(*kv, workspace, workspace_bytes);
+    if (st != SANTA_OK) return st;
+    *p = base_params(*kv, q, out, lse, workspace);
+    p->M = M;
+    p->mode = kModeSanta;
+    // The union of G heads' draws has at most min(K, G * M) teams.
+    const int64_t union_max = std::min<int64_t>(p->P, int64_t(p->G) * M);
+    p->tps = teams_per_split(int64_t(p->B) * p->Hkv * union_max);
+    p->max_splits = int32_t((union_max + p->tps - 1) / p->tps);
+    return SANTA_OK;
+}
+
+santa_status santa_select_teams(const santa_kv *kv, const void *q, const void *reps,
+                                int32_t M, uint64_t seed, uint32_t offset,
+                                int32_t *sampled, float *inv_pi,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    Params p;
+    santa_status st = santa_params(kv, q, M, nullptr, nullptr, workspace, workspace_bytes, &p);
+    if (st != SANTA_OK) return st;
+    if (!reps) return SANTA_ERR_NULL;
+    if ((sampled == nullptr) != (inv_pi == nullptr)) return SANTA_ERR_NULL;
+    p.reps = reps;
+    p.seed_lo = uint32_t(seed & 0xffffffffu);
+    p.seed_hi = uint32_t(seed >> 32);
+    p.offset = offset;
+    p.sampled = sampled;
+    p.inv_pi = inv_pi;
+    return launch_select(p, stream);
+}
+
+santa_status santa_attend_selected(const santa_kv *kv, const void *q, int32_t M,
+                                   float *out, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    Params p;
+    santa_status st = santa_params(kv, q, M, out, lse, workspace, workspace_bytes, &p);
+    if (st != SANTA_OK) return st;
+    if (!out) return SANTA_ERR_NULL;
+    return run_gather_combine(p, stream);
+}
+
+santa_status santa_decode_attention(const santa_kv *kv, const void *q, const void *reps,
+                                    int32_t M, uint64_t seed, uint32_t offset,
+                                    float *out, float *lse, int32_t *sampled, float *inv_pi,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!q || !reps || !out) return SANTA_ERR_NULL;
+    st = santa_select_teams(kv, q, reps, M, seed, offset, sampled, inv_pi, workspace, workspace_bytes, stream);
+    if (st != SANTA_OK) return st;
+    return santa_attend_selected(kv, q, M, out, lse, workspace, workspace_bytes, stream);
+}
+
+santa_status dense_decode_attention(const santa_kv *kv, const void *q, float *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!q || !out) return SANTA_ERR_NULL;
+    st = check_workspace(*kv, workspace, workspace_bytes);
+    if (st != SANTA_OK) return st;
+    Params p = base_params(*kv, q, out, lse, workspace);
+    p.mode = kModeDense;
+    p.tps = teams_per_split(int64_t(p.B) * p.Hkv * p.P);
+    p.max_splits = (p.P + p.tps - 1) / p.tps;
+    return run_gather_combine(p, stream);
+}
+
+santa_status santa_attention_given_teams(const santa_kv *kv, const void *q, int32_t M,
+                                         const int32_t *teams, const float *weights,
+                                         float *out, float *lse,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+    Params p;
+    santa_status st = santa_params(kv, q, M, out, lse, workspace, workspace_bytes, &p);
+    if (st != SANTA_OK) return st;
+    if (!teams || !weights || !out) return SANTA_ERR_NULL;
+    p.given_teams = teams;
+    p.given_w = weights;
+    st = launch_given(p, stream);
+    if (st != SANTA_OK) return st;
+    return run_gather_combine(p, stream);
+}
+
+const char *santa_status_string(int32_t status) {
+    switch (status) {
+        case SANTA_OK: return "ok";
+        case SANTA_ERR_NULL: return "a required pointer is NULL";
+        case SANTA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+        case SANTA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, page_size or group size";
+        case SANTA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SANTA_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t santa_version(void) { return 100; }
+
+}  // extern "C"

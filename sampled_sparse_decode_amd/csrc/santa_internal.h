@@ -1,0 +1,72 @@
+// Internal interface between the host entry points (santa_api.cpp) and the
+// HIP kernels (santa_kernels.hip). Not installed; not part of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/santa.h"
+
+namespace santa {
+
+constexpr int kMaxTeams = 2048;        // max_pages_per_seq limit (LDS-resident scan)
+constexpr int kMaxWords = kMaxTeams / 32;
+constexpr int kMaxGroup = 16;          // query heads per KV head
+constexpr int kMaxTeamsPerSplit = 16;
+
+enum Mode : int32_t { kModeSanta = 0, kModeDense = 1 };
+
+// Byte offsets of the workspace sections (all 256-byte aligned).
+struct WorkspaceLayout {
+    size_t bitmaps;     // uint32 [B][Hq][words]      team bitmap of each query head
+    size_t lnw;         // float  [B][Hq][P]          log weight of each drawn team
+    size_t part_ml;     // float2 [B][Hq][P]          split partial (max, sum)
+    size_t part_acc;    // float  [B][Hq][P][d]       split partial weighted value sums
+    size_t total;
+    int32_t words;      // ceil(P / 32)
+    int32_t max_splits; // P
+};
+
+WorkspaceLayout workspace_layout(const santa_kv &kv);
+
+// Everything a kernel launch needs, passed by value.
+struct Params {
+    const void *k_pages;
+    const void *v_pages;
+    const void *q;
+    const void *reps;
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    int64_t num_pages;
+    int32_t dtype;
+    int32_t B, Hq, Hkv, G, d, T, P, words;
+    int32_t M;
+    uint32_t seed_lo, seed_hi, offset;
+    int32_t mode;           // Mode
+    int32_t tps;            // union teams per split-K block
+    int32_t max_splits;     // gather grid.x
+    double scale;           // 1 / sqrt(d)
+    uint32_t *bitmaps;
+    float *lnw;
+    float *part_ml;         // float2 pairs
+    float *part_acc;
+    float *out;
+    float *lse;
+    int32_t *sampled;
+    float *inv_pi;
+    const int32_t *given_teams;
+    const float *given_w;
+    void *reps_out;
+};
+
+// Host-side argument checks; no HIP calls.
+santa_status validate_kv(const santa_kv *kv);
+
+// Kernel launches (santa_kernels.hip). Each returns SANTA_OK or SANTA_ERR_HIP.
+santa_status launch_build_reps(const Params &p, void *stream);
+santa_status launch_select(const Params &p, void *stream);
+santa_status launch_given(const Params &p, void *stream);
+santa_status launch_gather(const Params &p, void *stream);
+santa_status launch_combine(const Params &p, void *stream);
+
+}  // namespace santa

@@ -1,0 +1,270 @@
+"""ctypes binding of libsanta (include/santa.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors become device pointers, the
+current torch stream becomes the HIP stream, and a non-zero status becomes a
+``SantaError``. Every step of the computation runs in the library's HIP
+kernels; there is no fallback path, and a missing library raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsanta.so")
+
+SANTA_F32 = 0
+SANTA_BF16 = 1
+_DTYPES = {torch.float32: SANTA_F32, torch.bfloat16: SANTA_BF16}
+
+EXPORTED = (
+    "santa_workspace_size",
+    "santa_build_reps",
+    "santa_decode_attention",
+    "santa_select_teams",
+    "santa_attend_selected",
+    "dense_decode_attention",
+    "santa_attention_given_teams",
+    "santa_status_string",
+    "santa_version",
+)
+
+
+class SantaError(RuntimeError):
+    """A libsanta entry point returned a non-zero status."""
+
+    def __init__(self, func, status, text):
+        super().__init__(f"{func} failed with status {status}: {text}")
+        self.status = status
+
+
+class santa_kv(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load libsanta.so (built in-tree) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m sampled_sparse_decode_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    kvp = ctypes.POINTER(santa_kv)
+    i32, u32, u64, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t
+    sigs = {
+        "santa_workspace_size": (i32, [kvp, i32, ctypes.POINTER(sz)]),
+        "santa_build_reps": (i32, [kvp, P, P]),
+        "santa_decode_attention": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P, sz, P]),
+        "santa_select_teams": (i32, [kvp, P, P, i32, u64, u32, P, P, P, sz, P]),
+        "santa_attend_selected": (i32, [kvp, P, i32, P, P, P, sz, P]),
+        "dense_decode_attention": (i32, [kvp, P, P, P, P, sz, P]),
+        "santa_attention_given_teams": (i32, [kvp, P, i32, P, P, P, P, P, sz, P]),
+        "santa_status_string": (ctypes.c_char_p, [i32]),
+        "santa_version": (i32, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def santa_status_string(status):
+    return load().santa_status_string(int(status)).decode()
+
+
+def santa_version():
+    return load().santa_version()
+
+
+def _check(func, status):
+    if status != 0:
+        raise SantaError(func, status, santa_status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class KVCache:
+    """A paged KV cache on the device, in the layout of include/santa.h.
+
+    k_pages, v_pages: [num_pages][Hkv][T][d] bfloat16 or float32 tensors;
+    page_table [B][max_pages_per_seq] int32; seq_lens [B] int32.
+    """
+
+    def __init__(self, k_pages, v_pages, page_table, seq_lens, num_q_heads):
+        for t in (k_pages, v_pages, page_table, seq_lens):
+            if not t.is_contiguous():
+                raise ValueError("KV cache tensors must be contiguous")
+        if k_pages.dtype not in _DTYPES or v_pages.dtype != k_pages.dtype:
+            raise ValueError("k_pages / v_pages must both be bfloat16 or float32")
+        if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+            raise ValueError("page_table and seq_lens must be int32")
+        if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
+            raise ValueError("k_pages and v_pages must be [num_pages][Hkv][T][d]")
+        self.k_pages, self.v_pages = k_pages, v_pages
+        self.page_table, self.seq_lens = page_table, seq_lens
+        self.num_q_heads = int(num_q_heads)
+        self.num_pages, self.num_kv_heads, self.page_size, self.head_dim = (int(x) for x in k_pages.shape)
+        self.batch, self.max_pages_per_seq = (int(x) for x in page_table.shape)
+        self.dtype = k_pages.dtype
+        self.device = k_pages.device
+
+    def desc(self):
+        return santa_kv(_DTYPES[self.dtype], self.batch, self.num_q_heads, self.num_kv_heads,
+                        self.head_dim, self.page_size, self.max_pages_per_seq, 0, self.num_pages,
+                        self.k_pages.data_ptr(), self.v_pages.data_ptr(),
+                        self.page_table.data_ptr(), self.seq_lens.data_ptr())
+
+
+def storage_tensor(arr, dtype, device):
+    """numpy storage array (uint16 bfloat16 bits or float32) -> torch tensor on ``device``."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def kv_from_workload(w, device="cuda"):
+    """Upload a workloads.Workload; returns (KVCache, q tensor)."""
+    kv = KVCache(storage_tensor(w.k_pages, w.dtype, device), storage_tensor(w.v_pages, w.dtype, device),
+                 torch.from_numpy(np.ascontiguousarray(w.page_table, dtype=np.int32)).to(device),
+                 torch.from_numpy(np.ascontiguousarray(w.seq_lens, dtype=np.int32)).to(device),
+                 w.num_q_heads)
+    return kv, storage_tensor(w.q, w.dtype, device)
+
+
+def santa_workspace_size(kv, M):
+    n = ctypes.c_size_t(0)
+    d = kv.desc()
+    _check("santa_workspace_size", load().santa_workspace_size(ctypes.byref(d), int(M), ctypes.byref(n)))
+    return n.value
+
+
+def make_workspace(kv, M=1):
+    return torch.empty(santa_workspace_size(kv, M), dtype=torch.uint8, device=kv.device)
+
+
+def santa_build_reps(kv, reps=None):
+    """Mean key per (page, KV head), rounded to the cache dtype: [num_pages][Hkv][d]."""
+    if reps is None:
+        reps = torch.zeros((kv.num_pages, kv.num_kv_heads, kv.head_dim), dtype=kv.dtype, device=kv.device)
+    d = kv.desc()
+    _check("santa_build_reps", load().santa_build_reps(ctypes.byref(d), _ptr(reps), _stream()))
+    return reps
+
+
+def _check_q(kv, q):
+    if q.dtype != kv.dtype or not q.is_contiguous() or tuple(q.shape) != (kv.batch, kv.num_q_heads, kv.head_dim):
+        raise ValueError("q must be a contiguous [B][Hq][d] tensor of the cache dtype")
+
+
+def santa_decode_attention(kv, q, reps, M, seed=0, offset=0, workspace=None, out=None, lse=None,
+                           return_sets=False):
+    """SANTA++ decode attention. Returns (out, lse) or (out, lse, sampled, inv_pi)."""
+    _check_q(kv, q)
+    B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
+    dev = kv.device
+    if workspace is None:
+        workspace = make_workspace(kv, M)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    sampled = inv_pi = None
+    if return_sets:
+        sampled = torch.empty((B, Hq, M), dtype=torch.int32, device=dev)
+        inv_pi = torch.empty((B, Hq, M), dtype=torch.float32, device=dev)
+    desc = kv.desc()
+    st = load().santa_decode_attention(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed), int(offset),
+                                       _ptr(out), _ptr(lse), _ptr(sampled), _ptr(inv_pi),
+                                       _ptr(workspace), workspace.numel(), _stream())
+    _check("santa_decode_attention", st)
+    if return_sets:
+        return out, lse, sampled, inv_pi
+    return out, lse
+
+
+def santa_select_teams(kv, q, reps, M, seed, offset, workspace, sampled=None, inv_pi=None):
+    """Steps 1-4 of SANTA++ into ``workspace`` (and sampled / inv_pi when given)."""
+    _check_q(kv, q)
+    desc = kv.desc()
+    st = load().santa_select_teams(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed), int(offset),
+                                   _ptr(sampled), _ptr(inv_pi), _ptr(workspace), workspace.numel(), _stream())
+    _check("santa_select_teams", st)
+
+
+def santa_attend_selected(kv, q, M, workspace, out, lse=None):
+    """Step 5 of SANTA++ over the teams the last santa_select_teams left in ``workspace``."""
+    _check_q(kv, q)
+    desc = kv.desc()
+    st = load().santa_attend_selected(ctypes.byref(desc), _ptr(q), int(M), _ptr(out), _ptr(lse),
+                                      _ptr(workspace), workspace.numel(), _stream())
+    _check("santa_attend_selected", st)
+    return out, lse
+
+
+def dense_decode_attention(kv, q, workspace=None, out=None, lse=None):
+    """Dense decode attention over every cached token. Returns (out, lse)."""
+    _check_q(kv, q)
+    B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
+    if workspace is None:
+        workspace = make_workspace(kv, 1)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=kv.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=kv.device)
+    desc = kv.desc()
+    st = load().dense_decode_attention(ctypes.byref(desc), _ptr(q), _ptr(out), _ptr(lse),
+                                       _ptr(workspace), workspace.numel(), _stream())
+    _check("dense_decode_attention", st)
+    return out, lse
+
+
+def santa_attention_given_teams(kv, q, teams, weights, workspace=None, out=None, lse=None):
+    """Estimator over caller-chosen teams [B][Hq][M] (int32, -1 unused) and weights (float32)."""
+    _check_q(kv, q)
+    B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
+    M = int(teams.shape[-1])
+    if teams.dtype != torch.int32 or weights.dtype != torch.float32 or tuple(teams.shape) != (B, Hq, M) \
+            or tuple(weights.shape) != (B, Hq, M):
+        raise ValueError("teams must be int32 [B][Hq][M] and weights float32 [B][Hq][M]")
+    if workspace is None:
+        workspace = make_workspace(kv, M)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=kv.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=kv.device)
+    desc = kv.desc()
+    st = load().santa_attention_given_teams(ctypes.byref(desc), _ptr(q), M, _ptr(teams.contiguous()),
+                                            _ptr(weights.contiguous()), _ptr(out), _ptr(lse),
+                                            _ptr(workspace), workspace.numel(), _stream())
+    _check("santa_attention_given_teams", st)
+    return out, lse

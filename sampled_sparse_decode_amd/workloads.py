@@ -16,6 +16,8 @@ The workloads stand in for the KV caches of the model the SANTA++ abstract
 evaluates (Qwen2.5-7B-Instruct at 32K context: 28 query heads over 4 KV
 heads, head dimension 128); no model weights or evaluation data are used.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -71,30 +73,61 @@ def storage_to_f32(a, dtype):
     return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _contiguous(name, dtype, keys, vals, q, T, M, seed=0, offset=0, notes=None):
-    """Pack logical caches [B][Hkv][L][d] into identity-mapped pages.
+class _PagedBuilder:
+    """Identity-mapped paged cache filled one (sequence, KV head) at a time.
 
     Sequence b's team t sits at physical page b * P + t, P = ceil(L / T); a
     ragged tail is zero-padded (padding slots are never read).
     """
+
+    def __init__(self, B, hkv, L, T, d, dtype):
+        self.B, self.hkv, self.L, self.T, self.d, self.dtype = B, hkv, L, T, d, dtype
+        self.P = (L + T - 1) // T
+        esz = np.uint16 if dtype == "bf16" else np.float32
+        self.k = np.zeros((B * self.P, hkv, T, d), dtype=esz)
+        self.v = np.zeros((B * self.P, hkv, T, d), dtype=esz)
+
+    def put(self, which, b, g, x):
+        """Store float32 rows x [L][d] of sequence b, KV head g; returns the stored values as float32."""
+        P, T, d = self.P, self.T, self.d
+        buf = np.zeros((P * T, d), dtype=np.float32)
+        buf[:self.L] = x
+        st = to_storage(buf, self.dtype)
+        (self.k if which == "k" else self.v)[b * P:(b + 1) * P, g] = st.reshape(P, T, d)
+        return storage_to_f32(st[:self.L], self.dtype)
+
+    def workload(self, name, q, M, seed=0, offset=0, notes=None):
+        B, P = self.B, self.P
+        page_table = (np.arange(B, dtype=np.int32)[:, None] * P + np.arange(P, dtype=np.int32)[None, :])
+        return Workload(name=name, dtype=self.dtype, batch=B, num_q_heads=q.shape[1], num_kv_heads=self.hkv,
+                        head_dim=self.d, page_size=self.T, max_pages_per_seq=P, k_pages=self.k,
+                        v_pages=self.v, q=to_storage(q, self.dtype), page_table=page_table.astype(np.int32),
+                        seq_lens=np.full(B, self.L, dtype=np.int32), M=M, seed=seed, offset=offset,
+                        notes=notes or {})
+
+
+def _per_chunk(data_seed, B, hkv, fill):
+    """Run fill(b, g, rng) for every (sequence, KV head) chunk, in parallel.
+
+    Each chunk draws from its own generator, spawned from ``data_seed`` by
+    numpy's SeedSequence, so the result does not depend on thread timing.
+    """
+    seqs = np.random.SeedSequence(data_seed).spawn(B * hkv)
+    jobs = [(b, g, np.random.default_rng(seqs[b * hkv + g])) for b in range(B) for g in range(hkv)]
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda j: fill(*j), jobs))
+
+
+def _contiguous(name, dtype, keys, vals, q, T, M, seed=0, offset=0, notes=None):
+    """Pack logical caches keys, vals [B][Hkv][L][d] (float32) into identity-mapped pages."""
     B, hkv, L, d = keys.shape
-    P = (L + T - 1) // T
-    pad = P * T - L
-    if pad:
-        z = np.zeros((B, hkv, pad, d), dtype=np.float32)
-        keys = np.concatenate([keys, z], axis=2)
-        vals = np.concatenate([vals, z], axis=2)
-
-    def pages(x):
-        x = x.reshape(B, hkv, P, T, d).transpose(0, 2, 1, 3, 4)
-        return to_storage(x.reshape(B * P, hkv, T, d), dtype)
-
-    page_table = (np.arange(B, dtype=np.int32)[:, None] * P + np.arange(P, dtype=np.int32)[None, :]).astype(np.int32)
-    return Workload(name=name, dtype=dtype, batch=B, num_q_heads=q.shape[1], num_kv_heads=hkv,
-                    head_dim=d, page_size=T, max_pages_per_seq=P, k_pages=pages(keys),
-                    v_pages=pages(vals), q=to_storage(q, dtype), page_table=page_table,
-                    seq_lens=np.full(B, L, dtype=np.int32), M=M, seed=seed, offset=offset,
-                    notes=notes or {})
+    pb = _PagedBuilder(B, hkv, L, T, d, dtype)
+    for b in range(B):
+        for g in range(hkv):
+            pb.put("k", b, g, keys[b, g])
+            pb.put("v", b, g, vals[b, g])
+    return pb.workload(name, q, M, seed, offset, notes)
 
 
 def tiny_planted(data_seed=1, n=1024, d=64, T=32, M=8, dtype="f32", philox_seed=0):
@@ -130,20 +163,24 @@ def qwen_planted(data_seed=2, batch=1, seq_len=32768, T=128, M=31, hq=28, hkv=4,
     rng = np.random.default_rng(data_seed)
     G = hq // hkv
     scale = _channel_scales(rng, hkv, d)
-    keys = rng.standard_normal((batch, hkv, seq_len, d), dtype=np.float32) * scale[None, :, None, :]
-    vals = rng.standard_normal((batch, hkv, seq_len, d), dtype=np.float32)
     q = storage_to_f32(to_storage(rng.standard_normal((batch, hq, d), dtype=np.float32), dtype), dtype)
+    pb = _PagedBuilder(batch, hkv, seq_len, T, d, dtype)
     planted = {}
-    for b in range(batch):
-        for g in range(hkv):
-            pos = rng.choice(seq_len, size=min(G * plants, seq_len), replace=False)
-            for i in range(G):
-                h = g * G + i
-                ps = pos[i * plants:(i + 1) * plants]
-                keys[b, g, ps] = 2.0 * q[b, h][None, :] + 0.5 * rng.standard_normal((len(ps), d), dtype=np.float32)
-                planted[(b, h)] = sorted(int(x) for x in ps)
-    return _contiguous(f"qwen7b_{dtype}_b{batch}_n{seq_len}_t{T}_m{M}", dtype, keys, vals, q, T, M,
-                       seed=philox_seed, notes={"planted": planted})
+
+    def fill(b, g, r):
+        keys = r.standard_normal((seq_len, d), dtype=np.float32) * scale[g][None, :]
+        pos = r.choice(seq_len, size=min(G * plants, seq_len), replace=False)
+        for i in range(G):
+            h = g * G + i
+            ps = pos[i * plants:(i + 1) * plants]
+            keys[ps] = 2.0 * q[b, h][None, :] + 0.5 * r.standard_normal((len(ps), d), dtype=np.float32)
+            planted[(b, h)] = sorted(int(x) for x in ps)
+        pb.put("k", b, g, keys)
+        pb.put("v", b, g, r.standard_normal((seq_len, d), dtype=np.float32))
+
+    _per_chunk(data_seed, batch, hkv, fill)
+    return pb.workload(f"qwen7b_{dtype}_b{batch}_n{seq_len}_t{T}_m{M}", q, M, seed=philox_seed,
+                       notes={"planted": planted})
 
 
 def qwen_mixed_query(data_seed=3, batch=8, seq_len=32768, T=128, M=32, hq=28, hkv=4, d=128,
@@ -157,16 +194,19 @@ def qwen_mixed_query(data_seed=3, batch=8, seq_len=32768, T=128, M=32, hq=28, hk
     rng = np.random.default_rng(data_seed)
     G = hq // hkv
     scale = _channel_scales(rng, hkv, d)
-    keys = rng.standard_normal((batch, hkv, seq_len, d), dtype=np.float32) * scale[None, :, None, :]
-    keys = storage_to_f32(to_storage(keys, dtype), dtype)
-    vals = rng.standard_normal((batch, hkv, seq_len, d), dtype=np.float32)
     q = (1.0 - mix) * rng.standard_normal((batch, hq, d), dtype=np.float32)
-    picks = rng.integers(0, seq_len, size=(batch, hq))
-    for b in range(batch):
-        for h in range(hq):
-            q[b, h] += mix * keys[b, h // G, picks[b, h]]
-    return _contiguous(f"qwen7b_mixq_{dtype}_b{batch}_n{seq_len}_t{T}_m{M}", dtype, keys, vals,
-                       q.astype(np.float32), T, M, seed=philox_seed)
+    pb = _PagedBuilder(batch, hkv, seq_len, T, d, dtype)
+
+    def fill(b, g, r):
+        stored = pb.put("k", b, g, r.standard_normal((seq_len, d), dtype=np.float32) * scale[g][None, :])
+        picks = r.integers(0, seq_len, size=G)
+        for i in range(G):
+            q[b, g * G + i] += mix * stored[picks[i]]
+        pb.put("v", b, g, r.standard_normal((seq_len, d), dtype=np.float32))
+
+    _per_chunk(data_seed, batch, hkv, fill)
+    return pb.workload(f"qwen7b_mixq_{dtype}_b{batch}_n{seq_len}_t{T}_m{M}", q.astype(np.float32), M,
+                       seed=philox_seed)
 
 
 def gaussian_mixture(data_seed=4, batch=4, seq_len=131072, T=256, M=64, hq=28, hkv=4, d=128,
@@ -180,19 +220,22 @@ def gaussian_mixture(data_seed=4, batch=4, seq_len=131072, T=256, M=64, hq=28, h
     """
     rng = np.random.default_rng(data_seed)
     means = 2.0 * rng.standard_normal((hkv, components, d), dtype=np.float32)
-    keys = rng.standard_normal((batch, hkv, seq_len, d), dtype=np.float32)
-    for b in range(batch):
-        for g in range(hkv):
-            pos = 0
-            while pos < seq_len:
-                run = int(rng.integers(run_min, run_max + 1))
-                c = int(rng.integers(0, components))
-                keys[b, g, pos:pos + run] += means[g, c][None, :]
-                pos += run
-    vals = rng.standard_normal((batch, hkv, seq_len, d), dtype=np.float32)
     q = rng.standard_normal((batch, hq, d), dtype=np.float32)
-    return _contiguous(f"mixture_{dtype}_b{batch}_n{seq_len}_t{T}_m{M}", dtype, keys, vals, q, T, M,
-                       seed=philox_seed)
+    pb = _PagedBuilder(batch, hkv, seq_len, T, d, dtype)
+
+    def fill(b, g, r):
+        keys = r.standard_normal((seq_len, d), dtype=np.float32)
+        pos = 0
+        while pos < seq_len:
+            run = int(r.integers(run_min, run_max + 1))
+            c = int(r.integers(0, components))
+            keys[pos:pos + run] += means[g, c][None, :]
+            pos += run
+        pb.put("k", b, g, keys)
+        pb.put("v", b, g, r.standard_normal((seq_len, d), dtype=np.float32))
+
+    _per_chunk(data_seed, batch, hkv, fill)
+    return pb.workload(f"mixture_{dtype}_b{batch}_n{seq_len}_t{T}_m{M}", q, M, seed=philox_seed)
 
 
 def paged_ragged(data_seed=5, num_seqs=16, len_min=4096, len_max=65536, T=128, M=48, hq=28, hkv=4,
@@ -215,19 +258,22 @@ def paged_ragged(data_seed=5, num_seqs=16, len_min=4096, len_max=65536, T=128, M
     esz = np.uint16 if dtype == "bf16" else np.float32
     k_pages = np.zeros((total, hkv, T, d), dtype=esz)
     v_pages = np.zeros((total, hkv, T, d), dtype=esz)
-    start = 0
+    starts = np.concatenate([[0], np.cumsum(kb)[:-1]])
     for b in range(num_seqs):
+        page_table[b, :kb[b]] = perm[starts[b]:starts[b] + kb[b]]
+
+    def fill(b, g, r):
         L, K = int(lens[b]), int(kb[b])
-        ids = perm[start:start + K]
-        start += K
-        page_table[b, :K] = ids
-        keys = rng.standard_normal((hkv, K * T, d), dtype=np.float32) * scale[:, None, :]
-        keys[:, :sinks] *= sink_scale
-        keys[:, L:] = 0.0
-        vals = rng.standard_normal((hkv, K * T, d), dtype=np.float32)
-        vals[:, L:] = 0.0
-        k_pages[ids] = to_storage(keys.reshape(hkv, K, T, d).transpose(1, 0, 2, 3), dtype)
-        v_pages[ids] = to_storage(vals.reshape(hkv, K, T, d).transpose(1, 0, 2, 3), dtype)
+        ids = page_table[b, :K]
+        keys = r.standard_normal((K * T, d), dtype=np.float32) * scale[g][None, :]
+        keys[:sinks] *= sink_scale
+        keys[L:] = 0.0
+        vals = r.standard_normal((K * T, d), dtype=np.float32)
+        vals[L:] = 0.0
+        k_pages[ids, g] = to_storage(keys, dtype).reshape(K, T, d)
+        v_pages[ids, g] = to_storage(vals, dtype).reshape(K, T, d)
+
+    _per_chunk(data_seed, num_seqs, hkv, fill)
     q = rng.standard_normal((num_seqs, hq, d), dtype=np.float32)
     return Workload(name=f"paged_ragged_{dtype}_s{num_seqs}_t{T}_m{M}", dtype=dtype, batch=num_seqs,
                     num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=T, max_pages_per_seq=P,

@@ -1,0 +1,105 @@
+"""Shared comparison logic of the GPU parity tests: run the CPU oracle on the
+same seeded inputs and compare the HIP results with it, head by head.
+
+Tolerances (max-abs over every output element): 4e-3 for a bfloat16 cache
+with float32 accumulation, 1e-5 for a float32 cache. Team sets must match
+exactly, except that a draw whose uniform lies within 1e-6 of a CDF boundary
+(a near-tie, flagged by the oracle) may land on either neighbouring team;
+then the HIP output is compared with the oracle's estimate on the HIP set.
+"""
+import math
+
+import numpy as np
+
+from oracle import numerics, santa
+
+OUT_TOL = {"bf16": 4e-3, "f32": 1e-5}
+LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}
+INV_PI_RTOL = 1e-6
+
+
+def oracle_kv(w):
+    return santa.PagedKV(w.dtype, w.k_pages, w.v_pages, w.page_table, w.seq_lens)
+
+
+def pages_of(w, pairs):
+    """Physical pages read by the (b, h) pairs (all teams of each sequence)."""
+    out = set()
+    for b, _ in pairs:
+        K = santa.num_teams(int(w.seq_lens[b]), w.page_size)
+        out.update(int(x) for x in w.page_table[b][:K])
+    return out
+
+
+def oracle_reps(w, pairs=None):
+    pages = None if pairs is None else pages_of(w, pairs)
+    return santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype, pages=pages)
+
+
+def decoded_reps(gpu_reps, dtype):
+    arr = gpu_reps.cpu()
+    if dtype == "bf16":
+        import torch
+        return numerics.decode_bf16(arr.view(torch.int16).numpy().view(np.uint16))
+    return arr.numpy().astype(np.float64)
+
+
+def check_reps(w, gpu_reps, pairs=None):
+    ref = oracle_reps(w, pairs)
+    got = decoded_reps(gpu_reps, w.dtype)
+    pages = sorted(pages_of(w, pairs if pairs is not None else [(b, 0) for b in range(w.batch)]))
+    assert np.array_equal(got[pages], ref[pages]), "representatives differ from the oracle"
+    return ref
+
+
+def check_dense_head(w, kv, b, h, out, lse):
+    qh = numerics.decode(w.q[b, h], w.dtype)
+    ref_out, ref_lse = santa.dense_head(kv, qh, b, h, w.num_q_heads)
+    err = float(np.max(np.abs(out - ref_out)))
+    assert err <= OUT_TOL[w.dtype], f"dense (b={b}, h={h}) max-abs {err}"
+    _check_lse(w, lse, ref_lse, b, h)
+    return err
+
+
+def _check_lse(w, got, ref, b, h):
+    if ref == -math.inf:
+        assert got == -math.inf, f"(b={b}, h={h}) lse {got}, expected -inf"
+    else:
+        assert abs(got - ref) <= LSE_TOL[w.dtype] * max(1.0, abs(ref) / 16), f"(b={b}, h={h}) lse {got} vs {ref}"
+
+
+def check_santa_head(w, kv, reps, b, h, out, lse, teams, inv_pi, M=None, seed=None, offset=None):
+    """Compare one head's HIP sets, weights, output and lse with the oracle.
+
+    Returns (max-abs error, near_tie_flip: bool).
+    """
+    M = w.M if M is None else M
+    seed = w.seed if seed is None else seed
+    offset = w.offset if offset is None else offset
+    qh = numerics.decode(w.q[b, h], w.dtype)
+    res = santa.santa_head(kv, qh, reps, b, h, w.num_q_heads, M, seed, offset)
+    sel = res.selection
+    got_teams = [int(t) for t in teams if t >= 0]
+    assert all(t < 0 for t in teams[len(got_teams):]), "sampled list not -1 padded"
+    assert got_teams == sorted(set(got_teams)), "sampled list not ascending and unique"
+    flip = got_teams != sel.teams
+    if flip:
+        diff = set(got_teams) ^ set(sel.teams)
+        assert diff <= sel.near_tie_teams, (
+            f"(b={b}, h={h}) team sets differ outside near-ties: gpu-only "
+            f"{sorted(set(got_teams) - set(sel.teams))}, oracle-only {sorted(set(sel.teams) - set(got_teams))}")
+    if sel.full:
+        ref_w = [1.0] * len(got_teams)
+    else:
+        ref_w = [1.0 / santa.inclusion_probability(sel.p[t], M) for t in got_teams]
+    w_got = np.asarray(inv_pi[:len(got_teams)], dtype=np.float64)
+    assert np.all(np.abs(w_got - ref_w) <= INV_PI_RTOL * np.abs(ref_w) + 1e-30), f"(b={b}, h={h}) 1/pi differs"
+    assert np.all(np.asarray(inv_pi[len(got_teams):]) == 0.0)
+    if flip:
+        ref_out, ref_lse = santa.evaluate_given_set(kv, qh, b, h, w.num_q_heads, got_teams, ref_w)
+    else:
+        ref_out, ref_lse = res.out, res.lse
+    err = float(np.max(np.abs(out - ref_out))) if len(ref_out) else 0.0
+    assert err <= OUT_TOL[w.dtype], f"santa (b={b}, h={h}) max-abs {err}"
+    _check_lse(w, lse, ref_lse, b, h)
+    return err, flip

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/santa.h declares, sizes its workspace, and rejects bad arguments
+with the documented status before making any HIP call (so these run
+without a GPU; no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sampled_sparse_decode_amd import santa as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "santa.h")
+
+OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+FAKE = 0x10000      # non-NULL pointer value; never dereferenced by validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(S.LIB_PATH):
+        pytest.skip("libsanta.so not built")
+    return S.load()
+
+
+def kv(**over):
+    d = dict(dtype=S.SANTA_BF16, batch=2, num_q_heads=28, num_kv_heads=4, head_dim=128, page_size=128,
+             max_pages_per_seq=256, reserved=0, num_pages=512, k_pages=FAKE, v_pages=FAKE,
+             page_table=FAKE, seq_lens=FAKE)
+    d.update(over)
+    return S.santa_kv(**d)
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(S.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.santa_version() == 100
+    for code in range(6):
+        assert S.santa_status_string(code)
+    assert S.santa_status_string(99) == "unknown status"
+
+
+def test_workspace_size_layout(lib):
+    k = kv()
+    n = ctypes.c_size_t(0)
+    assert lib.santa_workspace_size(ctypes.byref(k), 31, ctypes.byref(n)) == OK
+    B, Hq, P, d = 2, 28, 256, 128
+
+    def a(x):
+        return (x + 255) // 256 * 256
+    words = (P + 31) // 32
+    expect = a(B * Hq * words * 4) + a(B * Hq * P * 4) + a(B * Hq * P * 8) + a(B * Hq * P * d * 4)
+    assert n.value == expect
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=7), UNSUP),
+    (dict(batch=0), SHAPE),
+    (dict(batch=70000), SHAPE),
+    (dict(num_q_heads=30), SHAPE),              # 30 % 4 != 0
+    (dict(num_q_heads=68), UNSUP),              # group of 17
+    (dict(head_dim=96), UNSUP),
+    (dict(page_size=48), UNSUP),
+    (dict(max_pages_per_seq=0), SHAPE),
+    (dict(max_pages_per_seq=4096), SHAPE),
+    (dict(reserved=1), SHAPE),
+    (dict(num_pages=0), SHAPE),
+    (dict(k_pages=None), NULL),
+    (dict(page_table=None), NULL),
+    (dict(seq_lens=None), NULL),
+])
+def test_validation_rejects(lib, over, code):
+    k = kv(**over)
+    n = ctypes.c_size_t(0)
+    assert lib.santa_workspace_size(ctypes.byref(k), 8, ctypes.byref(n)) == code
+    assert lib.santa_build_reps(ctypes.byref(k), FAKE, None) == code
+    assert lib.dense_decode_attention(ctypes.byref(k), FAKE, FAKE, None, FAKE, 1 << 40, None) == code
+    assert lib.santa_decode_attention(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, FAKE, None, None, None,
+                                      FAKE, 1 << 40, None) == code
+
+
+def test_null_descriptor(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.santa_workspace_size(None, 8, ctypes.byref(n)) == NULL
+    assert lib.santa_decode_attention(None, FAKE, FAKE, 8, 0, 0, FAKE, None, None, None, FAKE, 1, None) == NULL
+
+
+def test_decode_argument_checks(lib):
+    k = kv()
+    big = 1 << 40
+    call = lib.santa_decode_attention
+    assert call(ctypes.byref(k), None, FAKE, 8, 0, 0, FAKE, None, None, None, FAKE, big, None) == NULL
+    assert call(ctypes.byref(k), FAKE, None, 8, 0, 0, FAKE, None, None, None, FAKE, big, None) == NULL
+    assert call(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, None, None, None, None, FAKE, big, None) == NULL
+    assert call(ctypes.byref(k), FAKE, FAKE, 0, 0, 0, FAKE, None, None, None, FAKE, big, None) == SHAPE
+    # sampled and inv_pi come together
+    assert call(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, FAKE, None, FAKE, None, FAKE, big, None) == NULL
+    # workspace missing or short
+    assert call(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, FAKE, None, None, None, None, big, None) == WS
+    n = ctypes.c_size_t(0)
+    lib.santa_workspace_size(ctypes.byref(k), 8, ctypes.byref(n))
+    assert call(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, FAKE, None, None, None, FAKE, n.value - 1, None) == WS
+    assert lib.dense_decode_attention(ctypes.byref(k), FAKE, FAKE, None, FAKE, n.value - 1, None) == WS
+    assert lib.santa_attention_given_teams(ctypes.byref(k), FAKE, 8, FAKE, FAKE, FAKE, None, FAKE,
+                                           n.value - 1, None) == WS
+    assert lib.santa_attention_given_teams(ctypes.byref(k), FAKE, 8, None, FAKE, FAKE, None, FAKE,
+                                           big, None) == NULL
+    assert lib.santa_attention_given_teams(ctypes.byref(k), FAKE, 0, FAKE, FAKE, FAKE, None, FAKE,
+                                           big, None) == SHAPE
+    assert lib.santa_build_reps(ctypes.byref(k), None, None) == NULL

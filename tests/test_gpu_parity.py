@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case prints what it runs (workload, shape, entry point) before its
+first GPU call. Small cases compare every head; the full-size workloads
+compare a sample of heads that the oracle evaluates one by one, in the same
+launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import santa as osanta
+from sampled_sparse_decode_amd import santa as S
+from sampled_sparse_decode_amd import workloads as W
+
+import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.load()          # a missing library fails here, loudly
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+SMALL = {
+    "tiny_f32": lambda: W.tiny_planted(),
+    "qwen_bf16_ragged": lambda: W.qwen_planted(batch=1, seq_len=4096 + 77, M=31),
+    "qwen_mixq_b2": lambda: W.qwen_mixed_query(batch=2, seq_len=8192, M=32),
+    "mixture_t256": lambda: W.gaussian_mixture(batch=2, seq_len=8192 + 100, T=256, M=16),
+    "paged_ragged": lambda: W.paged_ragged(num_seqs=4, len_min=300, len_max=9000, M=20),
+    "bf16_d64_t16_g16": lambda: W.qwen_planted(batch=2, seq_len=1000, T=16, M=12, hq=16, hkv=1, d=64,
+                                               plants=2),
+    "f32_d128_t64_g2": lambda: W.qwen_planted(batch=2, seq_len=3000, T=64, M=9, hq=4, hkv=2, d=128,
+                                              plants=3, dtype="f32"),
+    "f32_d64_t256_g8": lambda: W.gaussian_mixture(batch=1, seq_len=5000, T=256, M=6, hq=8, hkv=1, d=64,
+                                                  run_min=32, run_max=600, dtype="f32"),
+}
+
+
+def run_santa(w, kv, q, reps, M=None, seed=None, offset=None):
+    out, lse, teams, inv_pi = S.santa_decode_attention(
+        kv, q, reps, w.M if M is None else M, w.seed if seed is None else seed,
+        w.offset if offset is None else offset, return_sets=True)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), teams.cpu().numpy(), inv_pi.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_build_reps_bit_exact(name):
+    w = SMALL[name]()
+    say(f"[build_reps] {name} B={w.batch} P={w.num_pages} T={w.page_size} d={w.head_dim} {w.dtype}")
+    kv, _ = S.kv_from_workload(w)
+    reps = S.santa_build_reps(kv)
+    torch.cuda.synchronize()
+    parity.check_reps(w, reps)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_dense_parity(name):
+    w = SMALL[name]()
+    say(f"[dense] {name} B={w.batch} Hq={w.num_q_heads} L={list(w.seq_lens)} {w.dtype}")
+    kv, q = S.kv_from_workload(w)
+    out, lse = S.dense_decode_attention(kv, q)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    okv = parity.oracle_kv(w)
+    for b in range(w.batch):
+        for h in range(w.num_q_heads):
+            parity.check_dense_head(w, okv, b, h, out[b, h], lse[b, h])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_given_teams_parity(name):
+    """The estimator (gather + combine) alone, on the oracle's own team sets."""
+    w = SMALL[name]()
+    say(f"[given_teams] {name}")
+    okv = parity.oracle_kv(w)
+    reps = parity.oracle_reps(w)
+    from oracle import numerics
+    B, Hq, M = w.batch, w.num_q_heads, w.M
+    teams = np.full((B, Hq, M), -1, dtype=np.int32)
+    wts = np.zeros((B, Hq, M), dtype=np.float32)
+    refs = {}
+    for b in range(B):
+        for h in range(Hq):
+            qh = numerics.decode(w.q[b, h], w.dtype)
+            r = osanta.santa_head(okv, qh, reps, b, h, Hq, M, w.seed, w.offset)
+            n = len(r.selection.teams)
+            teams[b, h, :n] = r.selection.teams
+            wts[b, h, :n] = np.float32(r.selection.inv_pi)
+            # the oracle re-evaluated with the float32 weights the kernel receives
+            refs[(b, h)] = osanta.evaluate_given_set(okv, qh, b, h, Hq, r.selection.teams,
+                                                     [float(x) for x in wts[b, h, :n]])
+    kv, q = S.kv_from_workload(w)
+    out, lse = S.santa_attention_given_teams(kv, q, torch.from_numpy(teams).cuda(), torch.from_numpy(wts).cuda())
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for (b, h), (ro, rl) in refs.items():
+        err = float(np.max(np.abs(out[b, h] - ro)))
+        assert err <= parity.OUT_TOL[w.dtype], f"(b={b}, h={h}) max-abs {err}"
+        parity._check_lse(w, lse[b, h], rl, b, h)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_santa_parity(name):
+    w = SMALL[name]()
+    say(f"[santa] {name} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} M={w.M} T={w.page_size} {w.dtype}")
+    kv, q = S.kv_from_workload(w)
+    reps_gpu = S.santa_build_reps(kv)
+    out, lse, teams, inv_pi = run_santa(w, kv, q, reps_gpu)
+    reps = parity.check_reps(w, reps_gpu)
+    okv = parity.oracle_kv(w)
+    flips = 0
+    for b in range(w.batch):
+        for h in range(w.num_q_heads):
+            _, f = parity.check_santa_head(w, okv, reps, b, h, out[b, h], lse[b, h], teams[b, h], inv_pi[b, h])
+            flips += f
+    say(f"  near-tie flips: {flips}")
+
+
+def test_santa_deterministic_and_seeded():
+    w = SMALL["qwen_mixq_b2"]()
+    say("[determinism] qwen_mixq_b2")
+    kv, q = S.kv_from_workload(w)
+    reps = S.santa_build_reps(kv)
+    a = run_santa(w, kv, q, reps)
+    b = run_santa(w, kv, q, reps)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    c = run_santa(w, kv, q, reps, offset=1)
+    assert not np.array_equal(a[2], c[2])
+    d1, _ = S.dense_decode_attention(kv, q)
+    d2, _ = S.dense_decode_attention(kv, q)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2)
+
+
+def test_paged_permutation_invariance():
+    w = SMALL["paged_ragged"]()
+    say("[permutation] paged_ragged")
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(w.num_pages)
+    k2, v2 = np.empty_like(w.k_pages), np.empty_like(w.v_pages)
+    k2[perm], v2[perm] = w.k_pages, w.v_pages
+    kv1, q = S.kv_from_workload(w)
+    w.k_pages, w.v_pages, w.page_table = k2, v2, perm[w.page_table].astype(np.int32)
+    kv2, _ = S.kv_from_workload(w)
+    a = run_santa(w, kv1, q, S.santa_build_reps(kv1))
+    b = run_santa(w, kv2, q, S.santa_build_reps(kv2))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_edge_cases_empty_short_full_and_single_draw():
+    w = W.paged_ragged(num_seqs=5, len_min=200, len_max=3000, M=4, hq=8, hkv=2, T=64)
+    w.seq_lens[0] = 0          # empty sequence
+    w.seq_lens[1] = 1          # one token
+    w.seq_lens[2] = 64 * 3     # exactly K = 3 <= M: full coverage
+    say(f"[edge] lens={list(w.seq_lens)} M in (1, 4)")
+    kv, q = S.kv_from_workload(w)
+    reps_gpu = S.santa_build_reps(kv)
+    reps = parity.check_reps(w, reps_gpu)
+    okv = parity.oracle_kv(w)
+    for M in (1, 4):
+        out, lse, teams, inv_pi = run_santa(w, kv, q, reps_gpu, M=M)
+        for b in range(w.batch):
+            for h in range(w.num_q_heads):
+                parity.check_santa_head(w, okv, reps, b, h, out[b, h], lse[b, h], teams[b, h], inv_pi[b, h], M=M)
+        assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+        assert np.all(teams[0] == -1)
+    dout, dlse = S.dense_decode_attention(kv, q)
+    torch.cuda.synchronize()
+    dout, dlse = dout.cpu().numpy(), dlse.cpu().numpy()
+    for b in range(w.batch):
+        for h in range(w.num_q_heads):
+            parity.check_dense_head(w, okv, b, h, dout[b, h], dlse[b, h])
+
+
+FULL = {
+    "tiny_f32_n1024_m8": None,                                   # every head
+    "qwen7b_32k_b1_m31": [(0, 0), (0, 6), (0, 13), (0, 27)],
+    "qwen7b_32k_b8_m32": [(0, 1), (3, 14), (7, 27)],
+    "qwen7b_32k_b8_m64": [(1, 2), (6, 20)],
+    "mixture_128k_b4_t256_m64": [(0, 3), (3, 25)],
+    "paged_ragged_16seq_m48": [(0, 0), (5, 9), (11, 17), (15, 27)],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_heads(name):
+    w = W.FULL_SIZE[name]()
+    pairs = FULL[name] or [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
+    say(f"[full] {name} B={w.batch} P={w.num_pages} T={w.page_size} M={w.M} heads={pairs}")
+    kv, q = S.kv_from_workload(w)
+    reps_gpu = S.santa_build_reps(kv)
+    out, lse, teams, inv_pi = run_santa(w, kv, q, reps_gpu)
+    dout, dlse = S.dense_decode_attention(kv, q)
+    torch.cuda.synchronize()
+    dout, dlse = dout.cpu().numpy(), dlse.cpu().numpy()
+    reps = parity.check_reps(w, reps_gpu, pairs)
+    okv = parity.oracle_kv(w)
+    for b, h in pairs:
+        parity.check_santa_head(w, okv, reps, b, h, out[b, h], lse[b, h], teams[b, h], inv_pi[b, h])
+        parity.check_dense_head(w, okv, b, h, dout[b, h], dlse[b, h])
+    # Structural checks on every head: sets ascending, unique, in range; finite outputs.
+    for b in range(w.batch):
+        K = osanta.num_teams(int(w.seq_lens[b]), w.page_size)
+        for h in range(w.num_q_heads):
+            t = teams[b, h][teams[b, h] >= 0]
+            assert np.all(np.diff(t) > 0) and (len(t) == 0 or (t[0] >= 0 and t[-1] < K))
+            assert len(t) == (K if w.M >= K else len(t)) and len(t) <= min(K, w.M)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(dout))
