@@ -111,11 +111,7 @@ def cpu_baseline(w, budget_s):
     from oracle import numerics, santa as osanta
     kv = osanta.PagedKV(w.dtype, w.k_pages, w.v_pages, w.page_table, w.seq_lens)
     heads = [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
-    pages = set()
-    for b in range(w.batch):
-        K = osanta.num_teams(int(w.seq_lens[b]), w.page_size)
-        pages.update(int(x) for x in w.page_table[b][:K])
-    reps = osanta.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype, pages=pages)
+    reps = osanta.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
     qs = {bh: numerics.decode(w.q[bh], w.dtype) for bh in heads}
     done = 0
     t0 = time.perf_counter()

@@ -39,7 +39,12 @@
  *
  * Paged KV layout (all entry points)
  * ----------------------------------
- *   k_pages, v_pages  [num_pages][num_kv_heads][page_size][head_dim], dtype
+ *   k_pages           [num_pages][num_kv_heads][page_size][head_dim], dtype
+ *                     (token-major within a page)
+ *   v_pages           [num_pages][num_kv_heads][head_dim][page_size], dtype
+ *                     (channel-major within a page, the value layout of
+ *                     paged-attention caches: lets the matrix cores take the
+ *                     P V operand straight from HBM)
  *   page_table        [batch][max_pages_per_seq] int32: physical page of
  *                     logical team t of sequence b
  *   seq_lens          [batch] int32: cached tokens L_b of sequence b
@@ -88,7 +93,7 @@ typedef struct santa_kv {
     int32_t reserved;           /* must be 0                                         */
     int64_t num_pages;          /* physical pages in k_pages / v_pages               */
     const void *k_pages;        /* [num_pages][Hkv][T][d] dtype                      */
-    const void *v_pages;        /* [num_pages][Hkv][T][d] dtype                      */
+    const void *v_pages;        /* [num_pages][Hkv][d][T] dtype                      */
     const int32_t *page_table;  /* [B][max_pages_per_seq]                            */
     const int32_t *seq_lens;    /* [B], each in [0, T * max_pages_per_seq]           */
 } santa_kv;
@@ -101,20 +106,21 @@ typedef struct santa_kv {
  * validation status. */
 santa_status santa_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes);
 
-/* Representative keys: reps[p][g][:] = the mean of the keys of team p for KV
- * head g, rounded once (to nearest, ties to even) to the cache dtype.
- * [EXP] section 三 step 2 (one representative key per team: mean, medoid or
- * random are listed; the mean is used); [ABS] (the query scores one
- * representative from each team). The mean is the float64 sum of the n valid
- * keys divided by n (n < T only for a sequence's last team).
- *   reps  [num_pages][Hkv][d] dtype, written for every page some sequence
- *         references (team t < K_b); other pages are left untouched.
- * Run once after prefill and again after a page's keys change. */
+/* Representative keys: reps[b][t][g][:] = the mean of the keys of team t of
+ * sequence b for KV head g, rounded once (to nearest, ties to even) to the
+ * cache dtype. [EXP] section 三 step 2 (one representative key per team:
+ * mean, medoid or random are listed; the mean is used); [ABS] (the query
+ * scores one representative from each team). The mean is the float64 sum of
+ * the n valid keys divided by n (n < T only for a sequence's last team).
+ *   reps  [B][max_pages_per_seq][Hkv][d] dtype, indexed by logical team so
+ *         that selection reads it without a page-table lookup; written for
+ *         t < K_b, other rows left untouched.
+ * Run once after prefill, and for a team again after its keys change. */
 santa_status santa_build_reps(const santa_kv *kv, void *reps, void *stream);
 
 /* SANTA++ decode attention ([ABS]; [EXP] section 三 steps 2-7).
  * For each sequence b and query head h (KV head g):
- *   1. s_t = q . reps[page(b,t)][g] / sqrt(d), summed in float64;
+ *   1. s_t = q . reps[b][t][g] / sqrt(d), summed in float64;
  *   2. p = softmax(s) over the K_b teams, with cumulative sums C;
  *   3. M draws with replacement by inverse CDF: draw j takes word j mod 4 of
  *      Philox4x32-10 (Salmon et al., SC'11) with counter
@@ -129,7 +135,7 @@ santa_status santa_build_reps(const santa_kv *kv, void *reps, void *stream);
  * Draws are independent per query head; the K/V tiles of a KV head are read
  * once for the union of its query heads' drawn teams.
  *   q        [B][Hq][d] dtype
- *   reps     [num_pages][Hkv][d] dtype (from santa_build_reps)
+ *   reps     [B][max_pages_per_seq][Hkv][d] dtype (from santa_build_reps)
  *   M        draws per query head, >= 1
  *   seed     Philox key; offset: Philox counter word 3 (advance it per
  *            decode step and layer so every step draws afresh)

@@ -62,46 +62,37 @@ def team_size(L, T, t):
     return min(T, int(L) - t * T)
 
 
-def team_tokens(pages_f64, page_table_row, L, T, g, t):
-    """Rows [n_t][d] of team t of one sequence, KV head g, from the paged cache.
-
-    Layout: pages[physical_page][kv_head][slot][d]; team t of the sequence is
-    logical page t, stored at physical page page_table_row[t] (R1).
-    """
-    n = team_size(L, T, t)
-    return pages_f64[int(page_table_row[t]), g, :n, :]
-
-
 # ----------------------------------------------------------------------------
 # Representatives (reading R2)
 # ----------------------------------------------------------------------------
 
-def build_reps(k_pages, page_table, seq_lens, page_size, dtype, pages=None):
-    """Mean key of every referenced team, rounded once to the KV type.
+def build_reps(k_pages, page_table, seq_lens, page_size, dtype, seqs=None):
+    """Mean key of every team, rounded once to the KV type.
 
     [EXP] section 三 step 2: one representative key per team (mean, medoid or
     random are listed); [ABS]: the query scores one representative from each
     team. Reading R2: the mean, as math.fsum(column) / n (exact sum, one
     correctly rounded divide), then one round-to-nearest-even into the KV type.
 
-    Returns a float64 array [num_pages][Hkv][d]; pages no sequence references
-    (or not in ``pages`` when given) are NaN.
+    Returns a float64 array [B][max_pages][Hkv][d] indexed by logical team;
+    rows of teams past a sequence's end (or of sequences not in ``seqs`` when
+    given) are NaN.
     """
-    num_pages, hkv, T, d = k_pages.shape
-    reps = np.full((num_pages, hkv, d), np.nan)
-    want = None if pages is None else set(int(p) for p in pages)
-    for b in range(len(seq_lens)):
+    _, hkv, T, d = k_pages.shape
+    B, P = np.asarray(page_table).shape
+    reps = np.full((B, P, hkv, d), np.nan)
+    for b in range(B):
+        if seqs is not None and b not in seqs:
+            continue
         L = int(seq_lens[b])
         for t in range(num_teams(L, T)):
             p = int(page_table[b][t])
-            if want is not None and p not in want:
-                continue
             n = team_size(L, T, t)
             keys = decode(k_pages[p, :, :n, :], dtype)          # [Hkv][n][d]
             for g in range(hkv):
                 for c in range(d):
-                    reps[p, g, c] = math.fsum(keys[g, :, c]) / n
-            reps[p] = round_to_dtype(reps[p], dtype)
+                    reps[b, t, g, c] = math.fsum(keys[g, :, c]) / n
+            reps[b, t] = round_to_dtype(reps[b, t], dtype)
     return reps
 
 
@@ -276,9 +267,10 @@ def dense_attention(q_h, keys, vals):
 class PagedKV:
     """Float64 view of a paged KV cache as the library lays it out.
 
-    k_pages, v_pages: stored arrays [num_pages][Hkv][T][d] (uint16 bf16 bits
-    or float32); page_table [B][max_pages]; seq_lens [B]. Pages are decoded to
-    float64 on first use.
+    k_pages: stored array [num_pages][Hkv][T][d] (uint16 bf16 bits or
+    float32), token-major; v_pages: [num_pages][Hkv][d][T], channel-major
+    within a page; page_table [B][max_pages]; seq_lens [B]. Pages are decoded
+    to float64 on first use.
     """
 
     def __init__(self, dtype, k_pages, v_pages, page_table, seq_lens):
@@ -300,7 +292,7 @@ class PagedKV:
         p = int(self.page_table[b][t])
         n = team_size(L, self.T, t)
         return (self._page(self._k, self.k_raw, p)[g, :n, :],
-                self._page(self._v, self.v_raw, p)[g, :n, :])
+                self._page(self._v, self.v_raw, p)[g, :, :n].T)
 
     def all_tokens(self, b, g):
         L = int(self.seq_lens[b])
@@ -319,7 +311,7 @@ class HeadResult:
 def santa_head(kv, q_h, reps, b, h, num_q_heads, M, seed, offset):
     """SANTA++ for one (sequence b, query head h): select teams, then estimate.
 
-    q_h: float64 query [d]; reps: float64 [num_pages][Hkv][d] (from build_reps).
+    q_h: float64 query [d]; reps: float64 [B][max_pages][Hkv][d] (from build_reps).
     KV head of query head h is h // (Hq / Hkv) (grouped-query attention).
     """
     g = h // (num_q_heads // kv.hkv)
@@ -327,7 +319,7 @@ def santa_head(kv, q_h, reps, b, h, num_q_heads, M, seed, offset):
     K = num_teams(L, kv.T)
     if K == 0:
         return HeadResult(np.zeros(kv.d), -math.inf, Selection([], [], np.zeros(0), set(), [], True))
-    rep_rows = np.stack([reps[int(kv.page_table[b][t]), g] for t in range(K)])
+    rep_rows = np.stack([reps[b, t, g] for t in range(K)])
     sel = select_teams(q_h, rep_rows, M, seed, offset, b, h)
     out, lse = estimate(q_h, [kv.team(b, g, t) for t in sel.teams], sel.inv_pi)
     return HeadResult(out, lse, sel)

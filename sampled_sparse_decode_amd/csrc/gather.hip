@@ -1,0 +1,648 @@
+// Split-K gather over drawn teams and the cross-split combine (gfx950).
+//
+// Sources:
+//   [ABS] "SANTA++: Sampling Attention through Representative Keys",
+//         arXiv 2609.35629, abstract: exact attention scores inside the
+//         sampled teams; each team's contribution re-weighted by the inverse
+//         of its inclusion probability; the result estimates attention over
+//         the full cache.
+//   [EXP] "SANTA++：用代表性 Key 采样把 KV cache 读带宽砍掉 80%" (explainer),
+//         section 三 steps 4-5 (exact scores inside sampled teams, importance
+//         re-weighting).
+//
+// A gather block (split s, KV head g, sequence b) owns teams
+// [s * tps, (s + 1) * tps) of sequence b (tps divides 32, so their bits sit in
+// one bitmap word). It reads the group's bitmap word, the teams' log weights
+// and page ids in one round trip, keeps the teams some query head of g drew
+// (dense mode: every team, every head, weight 0 in log space), streams each
+// kept team's K and V tile from HBM exactly once, scores it for the heads that
+// drew it, and runs an online softmax in which the team weight w is folded
+// into the logit (s_j + log w): numerator and denominator both carry w, and
+// nothing overflows however large 1/pi gets. It writes one partial (max, sum,
+// weighted value sum) per head that drew a team of the split, at slot s. The
+// combine kernel reads the head's bitmap to know which slots hold partials and
+// merges them in split order. Blocks whose teams nobody drew exit after the
+// first round trip.
+//
+// Cache layout: K pages [page][g][T][d] (token-major), V pages [page][g][d][T]
+// (channel-major within a page), so that both matrix-core operands of the
+// bf16 path are plain 16-byte loads from HBM.
+#include "device_common.h"
+
+namespace santa {
+namespace {
+
+using namespace dev;
+
+constexpr int kGM = kMaxGroup;     // head slots per KV head (16)
+
+// Per-block team list, filled by load_team_list.
+struct TeamList {
+    int64_t page[kMaxTeamsPerSplit];
+    int32_t n[kMaxTeamsPerSplit];          // valid tokens of the team
+    float lnw[kMaxTeamsPerSplit][kGM];     // log weight per head slot, -inf if the head did not draw it
+    int32_t raw_page[kMaxTeamsPerSplit];
+    float raw_lnw[kMaxTeamsPerSplit][kGM];
+    uint32_t mask[kMaxTeamsPerSplit];      // heads that drew each team slot
+    uint32_t hword[kGM];                   // bitmap word of each head covering the block's teams
+    int32_t slot[kMaxTeamsPerSplit];       // team slot of each kept team
+    int32_t len;                           // clamped sequence length
+    int32_t nteams;
+};
+
+// Builds the block's team list in LDS with a single round trip to memory:
+// the sequence length, the teams' page ids, the heads' bitmap word and log
+// weights are all loaded before any is used. Returns the number of kept teams
+// (uniform over the block).
+__device__ int load_team_list(const Params &p, TeamList &tl, int s, int g, int b) {
+    const int tid = threadIdx.x;
+    const int G = p.G;
+    const int hbase = b * p.Hq + g * G;
+    const bool dense = p.mode == kModeDense;
+    const int i = tid / kGM, h = tid % kGM;          // team slot, head slot
+    const int t = s * p.tps + i;
+    const bool in = i < p.tps && t < p.P;
+    int32_t pg = 0;
+    float lw = kNegInfF;
+    uint32_t word = 0u;
+    if (in && h == 0) pg = p.page_table[size_t(b) * p.P + t];
+    if (!dense) {
+        if (in && h < G) lw = p.lnw[size_t(hbase + h) * p.P + t];
+        if (i == 0 && h < G) word = p.bitmaps[size_t(hbase + h) * p.words + (s * p.tps) / 32];
+    }
+    const int Lraw = p.seq_lens[b];
+    if (in) {
+        tl.raw_lnw[i][h] = lw;
+        if (h == 0) tl.raw_page[i] = pg;
+    }
+    if (i == 0) tl.hword[h] = word;
+    if (tid == 0) tl.len = clamp_len(Lraw, p.P * p.T);
+    __syncthreads();
+    const int L = tl.len;
+    const int K = (L + p.T - 1) / p.T;
+    if (tid < p.tps) {
+        const int tt = s * p.tps + tid;
+        uint32_t mask = 0u;
+        if (tt < K) {
+            if (dense) {
+                mask = (1u << G) - 1u;
+            } else {
+                for (int k = 0; k < G; ++k) mask |= ((tl.hword[k] >> (tt & 31)) & 1u) << k;
+            }
+        }
+        tl.mask[tid] = mask;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int n = 0;
+        for (int j = 0; j < p.tps; ++j)
+            if (tl.mask[j]) tl.slot[n++] = j;
+        tl.nteams = n;
+    }
+    __syncthreads();
+    const int nt = tl.nteams;
+    if (i < nt) {
+        const int j = tl.slot[i];
+        const int tt = s * p.tps + j;
+        if (h == 0) {
+            tl.page[i] = clamp_page(tl.raw_page[j], p.num_pages);
+            tl.n[i] = min(p.T, L - tt * p.T);
+        }
+        const bool drew = (tl.mask[j] >> h) & 1u;
+        tl.lnw[i][h] = drew ? (dense ? 0.0f : tl.raw_lnw[j][h]) : kNegInfF;
+    }
+    __syncthreads();
+    return nt;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 gather on the matrix cores.
+//
+// A wavefront processes 32-token chunks of the block's teams. For a chunk it
+// computes the score tile S^T (32 tokens x 16 head slots) as K Q^T with
+// v_mfma_f32_16x16x32_bf16 (fp32 accumulation of exact bf16 products); rows of
+// the two 16-row tiles are arranged so that lane l ends up holding, for head
+// (l mod 16), the scores of the 8 consecutive tokens 8 (l div 16) + 0..7.
+// That is exactly the A operand of the P V product for those tokens, and the
+// matching B operand is one 16-byte load of the channel-major V page. P is
+// split into a bfloat16 high part and a bfloat16 remainder so the product
+// keeps ~16 significant bits of P.
+// ---------------------------------------------------------------------------
+template <int D>
+struct MfmaChunk {
+    static constexpr int KS = D / 32;     // k-steps of K Q^T
+    static constexpr int NT = D / 16;     // channel tiles of P V
+    uint4 k[2][KS];
+    uint4 v[NT];
+};
+
+// Loads are unconditional: rows past the team's end are clamped to its last
+// valid row (K; those scores are masked) or to its first 8 tokens (V; zeroed
+// by keep_first), so every address stays inside the page and the wavefront
+// issues all of its loads back to back.
+template <int D>
+__device__ __forceinline__ void mfma_load_chunk(const Params &p, const TeamList &tl, int q, int cpt, int g,
+                                                int i16, int g4, MfmaChunk<D> &c) {
+    const int ti = q / cpt;
+    const int tb = (q - ti * cpt) * 32;
+    const int n = tl.n[ti];
+    const size_t tile = (size_t(tl.page[ti]) * p.Hkv + g) * size_t(p.T) * D;
+    const bf16_t *kt = static_cast<const bf16_t *>(p.k_pages) + tile;
+    const bf16_t *vt = static_cast<const bf16_t *>(p.v_pages) + tile;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int tok = tb + 8 * (i16 >> 2) + 4 * t + (i16 & 3);
+        const bf16_t *row = kt + size_t(min(tok, n - 1)) * D + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < MfmaChunk<D>::KS; ++ks) c.k[t][ks] = ld16(row + 32 * ks);
+    }
+    const int tok0 = tb + 8 * g4;
+    const bf16_t *col = vt + size_t(i16) * p.T + (tok0 < n ? tok0 : 0);
+#pragma unroll
+    for (int nt = 0; nt < MfmaChunk<D>::NT; ++nt) c.v[nt] = ld16(col + size_t(16 * nt) * p.T);
+}
+
+// Zero the bf16 elements e >= keep of a 16-byte operand (ragged team tails).
+__device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
+    if (keep >= 8) return v;
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e0 = 2 * i;
+        const uint32_t lo = (e0 < keep) ? 0x0000ffffu : 0u;
+        const uint32_t hi = (e0 + 1 < keep) ? 0xffff0000u : 0u;
+        w[i] &= (lo | hi);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int D>
+__device__ __forceinline__ void mfma_compute_chunk(const Params &p, const TeamList &tl, int q, int cpt,
+                                                   int i16, int g4, const bf16_t (*q_lds)[D + 8],
+                                                   const MfmaChunk<D> &c, float &m, float &lsum,
+                                                   f32x4 (&o)[D / 16]) {
+    const int ti = q / cpt;
+    const int tb = (q - ti * cpt) * 32;
+    const int n = tl.n[ti];
+    const float lw = tl.lnw[ti][i16];
+    const float scale = float(p.scale);
+
+    f32x4 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < MfmaChunk<D>::KS; ++ks)
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, c.k[t][ks]),
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&q_lds[i16][32 * ks + 8 * g4])), st[t],
+                0, 0, 0);
+    }
+    // Lane holds head i16, tokens tb + 8 g4 + j, j = 4 t + e.
+    float sc[8];
+    float cmax = kNegInfF;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int tok = tb + 8 * g4 + j;
+        const float x = st[j >> 2][j & 3] * scale + lw;
+        sc[j] = (tok < n && lw != kNegInfF) ? x : kNegInfF;
+        cmax = fmaxf(cmax, sc[j]);
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_old = m;
+    const float mnew = fmaxf(m, cmax);
+    const float corr = (m == kNegInfF) ? 0.0f : __expf(m - mnew);
+    float pj[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        pj[j] = (sc[j] == kNegInfF) ? 0.0f : __expf(sc[j] - mnew);
+        psum += pj[j];
+    }
+    lsum = lsum * corr + psum;
+    m = mnew;
+    // Rows of o are heads 4 g4 + e; their correction factors live in lanes
+    // 4 g4 + e. Skipped when no head's running max moved (or o is still zero).
+    if (__ballot(m_old != kNegInfF && corr != 1.0f) != 0ull) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float ce = __shfl(corr, 4 * g4 + e, 64);
+#pragma unroll
+            for (int nt = 0; nt < MfmaChunk<D>::NT; ++nt) o[nt][e] *= ce;
+        }
+    }
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        hb[j] = f32_to_bf16_rne(pj[j]);
+        lb[j] = f32_to_bf16_rne(pj[j] - __uint_as_float(hb[j] << 16));
+    }
+    const uint4 phu = make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
+                                 hb[6] | (hb[7] << 16));
+    const uint4 plu = make_uint4(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
+                                 lb[6] | (lb[7] << 16));
+    const bf16x8 ph = __builtin_bit_cast(bf16x8, phu);
+    const bf16x8 pl = __builtin_bit_cast(bf16x8, plu);
+    const int keep = n - (tb + 8 * g4);
+#pragma unroll
+    for (int nt = 0; nt < MfmaChunk<D>::NT; ++nt) {
+        const bf16x8 vv = __builtin_bit_cast(bf16x8, keep_first(c.v[nt], keep));
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vv, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vv, o[nt], 0, 0, 0);
+    }
+}
+
+template <int D, bool PREFETCH>
+__global__ __launch_bounds__(kBlock, PREFETCH ? 1 : 3) void gather_mfma_kernel(Params p) {
+    constexpr int KS = D / 32;
+    constexpr int NT = D / 16;
+    __shared__ TeamList tl;
+    __shared__ __attribute__((aligned(16))) bf16_t q_lds[kGM][D + 8];
+    __shared__ float red_m[kWaves][kGM];
+    __shared__ float red_l[kWaves][kGM];
+    __shared__ float red_o[kWaves][kGM][D];
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int G = p.G;
+    const int hbase = b * p.Hq + g * G;
+
+    // Q^T operand rows (head slots >= G are zero), kept in LDS and read per
+    // chunk; rows padded by 16 bytes so the 16 head rows hit different banks.
+    {
+        const int h = tid >> 4, cc = tid & 15;            // 16 heads x 16 chunks of 16 bytes
+        if (cc * 8 < D) {
+            const uint4 v = (h < G) ? ld16(static_cast<const bf16_t *>(p.q) + size_t(hbase + h) * D + cc * 8)
+                                    : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&q_lds[h][cc * 8]) = v;
+        }
+    }
+    const int nteams = load_team_list(p, tl, s, g, b);
+    if (nteams == 0) return;
+
+    const int cpt = p.T >= 32 ? p.T / 32 : 1;
+    const int nchunks = nteams * cpt;
+    float m = kNegInfF, lsum = 0.0f;
+    f32x4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if constexpr (PREFETCH) {
+        // Two chunk buffers in turn: the next chunk's loads are in flight
+        // while the current one is on the matrix cores.
+        MfmaChunk<D> ca, cb;
+        int q = wave;
+        if (q < nchunks) mfma_load_chunk<D>(p, tl, q, cpt, g, i16, g4, ca);
+        while (q < nchunks) {
+            const int q1 = q + kWaves;
+            if (q1 < nchunks) mfma_load_chunk<D>(p, tl, q1, cpt, g, i16, g4, cb);
+            mfma_compute_chunk<D>(p, tl, q, cpt, i16, g4, q_lds, ca, m, lsum, o);
+            if (q1 >= nchunks) break;
+            const int q2 = q1 + kWaves;
+            if (q2 < nchunks) mfma_load_chunk<D>(p, tl, q2, cpt, g, i16, g4, ca);
+            mfma_compute_chunk<D>(p, tl, q1, cpt, i16, g4, q_lds, cb, m, lsum, o);
+            q = q2;
+        }
+    } else {
+        // One chunk at a time; other resident blocks cover the load latency.
+        for (int q = wave; q < nchunks; q += kWaves) {
+            MfmaChunk<D> ck;
+            mfma_load_chunk<D>(p, tl, q, cpt, g, i16, g4, ck);
+            mfma_compute_chunk<D>(p, tl, q, cpt, i16, g4, q_lds, ck, m, lsum, o);
+        }
+    }
+
+    // Wavefront partials: sums over the four lane groups of a head.
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (g4 == 0) {
+        red_m[wave][i16] = m;
+        red_l[wave][i16] = lsum;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red_o[wave][4 * g4 + e][16 * nt + i16] = o[nt][e];
+    __syncthreads();
+
+    // Merge the wavefronts in a fixed order; one partial per head that drew a
+    // team of this split. The per-(head, wavefront) scale factors are
+    // computed once.
+    __shared__ float fac_s[kGM][kWaves];
+    __shared__ float hm_s[kGM], hl_s[kGM];
+    if (tid < G) {
+        const int h = tid;
+        float mx = red_m[0][h];
+        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, red_m[w][h]);
+        float l = 0.0f;
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = (red_m[w][h] == kNegInfF) ? 0.0f : expf(red_m[w][h] - mx);
+            fac_s[h][w] = f;
+            l += f * red_l[w][h];
+        }
+        hm_s[h] = mx;
+        hl_s[h] = l;
+    }
+    __syncthreads();
+    float2 *part_ml = reinterpret_cast<float2 *>(p.part_ml);
+    for (int idx = tid; idx < G * D; idx += kBlock) {
+        const int h = idx / D, c = idx - h * D;
+        if (hm_s[h] == kNegInfF) continue;          // the head drew no team of this split
+        const size_t slot = size_t(hbase + h) * p.P + s;
+        float a = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) a += fac_s[h][w] * red_o[w][h][c];
+        p.part_acc[slot * D + c] = a;
+        if (c == 0) part_ml[slot] = make_float2(hm_s[h], hl_s[h]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// float32 gather: scores in float64 (products of two float32 values are exact
+// in float64), one team at a time with block-wide steps. Used for float32
+// caches, where the 1e-5 output tolerance needs more than float32 scores.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kBlock) void gather_f32_kernel(Params p) {
+    constexpr int PARTS = kBlock / D;                   // token subsets per channel
+    constexpr int kMaxT = 256;
+    __shared__ TeamList tl;
+    __shared__ float q_s[kGM][D];
+    __shared__ double m_s[kGM], l_s[kGM], corr_s[kGM];
+    // Scores / weights of the current team, reused at the end for the
+    // per-part value sums (both 32 KiB).
+    __shared__ double buf[kGM * kMaxT];
+    static_assert(PARTS * kGM * D <= kGM * kMaxT, "reduction buffer fits the score buffer");
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int G = p.G;
+    const int hbase = b * p.Hq + g * G;
+    const float *qg = static_cast<const float *>(p.q) + size_t(hbase) * D;
+    for (int i = tid; i < kGM * D; i += kBlock) q_s[i / D][i % D] = (i / D < G) ? qg[i] : 0.0f;
+    if (tid < kGM) {
+        m_s[tid] = -INFINITY;
+        l_s[tid] = 0.0;
+    }
+    const int nteams = load_team_list(p, tl, s, g, b);
+    if (nteams == 0) return;
+
+    double (*sc)[kMaxT] = reinterpret_cast<double (*)[kMaxT]>(buf);
+    const int c = tid % D, part = tid / D;
+    double acc[kGM];
+#pragma unroll
+    for (int h = 0; h < kGM; ++h) acc[h] = 0.0;
+
+    for (int ti = 0; ti < nteams; ++ti) {
+        const int n = tl.n[ti];
+        const size_t tile = (size_t(tl.page[ti]) * p.Hkv + g) * size_t(p.T) * D;
+        const float *kt = static_cast<const float *>(p.k_pages) + tile;
+        const float *vt = static_cast<const float *>(p.v_pages) + tile;
+        for (int idx = tid; idx < n * G; idx += kBlock) {
+            const int j = idx / G, h = idx - j * G;
+            const float lw = tl.lnw[ti][h];
+            if (lw == kNegInfF) {
+                sc[h][j] = -INFINITY;
+                continue;
+            }
+            double dot = 0.0;
+            for (int c0 = 0; c0 < D; c0 += 4) {
+                const uint4 r = ld16(kt + size_t(j) * D + c0);
+                dot = fma(double(__uint_as_float(r.x)), double(q_s[h][c0 + 0]), dot);
+                dot = fma(double(__uint_as_float(r.y)), double(q_s[h][c0 + 1]), dot);
+                dot = fma(double(__uint_as_float(r.z)), double(q_s[h][c0 + 2]), dot);
+                dot = fma(double(__uint_as_float(r.w)), double(q_s[h][c0 + 3]), dot);
+            }
+            sc[h][j] = dot * p.scale + double(lw);
+        }
+        __syncthreads();
+        if (tid < G) {
+            const int h = tid;
+            if (tl.lnw[ti][h] == kNegInfF) {
+                corr_s[h] = 1.0;
+            } else {
+                double tm = -INFINITY;
+                for (int j = 0; j < n; ++j) tm = fmax(tm, sc[h][j]);
+                const double mn = fmax(m_s[h], tm);
+                corr_s[h] = (m_s[h] == -INFINITY) ? 0.0 : exp(m_s[h] - mn);
+                m_s[h] = mn;
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < n * G; idx += kBlock) {
+            const int j = idx / G, h = idx - j * G;
+            sc[h][j] = (tl.lnw[ti][h] == kNegInfF) ? 0.0 : exp(sc[h][j] - m_s[h]);
+        }
+        __syncthreads();
+        if (tid < G) {
+            double sum = 0.0;
+            for (int j = 0; j < n; ++j) sum += sc[tid][j];
+            l_s[tid] = l_s[tid] * corr_s[tid] + sum;
+        }
+#pragma unroll
+        for (int h = 0; h < kGM; ++h)
+            if (h < G) acc[h] *= corr_s[h];
+        for (int j = part; j < n; j += PARTS) {
+            const double v = double(vt[size_t(c) * p.T + j]);
+#pragma unroll
+            for (int h = 0; h < kGM; ++h)
+                if (h < G) acc[h] = fma(sc[h][j], v, acc[h]);
+        }
+        __syncthreads();
+    }
+    double (*red)[kGM][D] = reinterpret_cast<double (*)[kGM][D]>(buf);
+#pragma unroll
+    for (int h = 0; h < kGM; ++h)
+        if (h < G) red[part][h][c] = acc[h];
+    __syncthreads();
+    float2 *part_ml = reinterpret_cast<float2 *>(p.part_ml);
+    for (int idx = tid; idx < G * D; idx += kBlock) {
+        const int h = idx / D, cc = idx - h * D;
+        const size_t slot = size_t(hbase + h) * p.P + s;
+        if (m_s[h] == -INFINITY) continue;     // the head drew no team of this split
+        double a = 0.0;
+        for (int pp = 0; pp < PARTS; ++pp) a += red[pp][h][cc];
+        // Store relative to the float32-rounded max the partial is labelled with.
+        const float mstore = float(m_s[h]);
+        const double f = exp(m_s[h] - double(mstore));
+        p.part_acc[slot * D + cc] = float(a * f);
+        if (cc == 0) part_ml[slot] = make_float2(mstore, float(l_s[h] * f));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// combine: one 512-thread block per (sequence, query head). The head's bitmap
+// says which split slots hold its partials; they are merged in slot order:
+//   out = sum_s e^{m_s - m*} acc_s / sum_s e^{m_s - m*} l_s,
+//   lse = m* + log(sum_s e^{m_s - m*} l_s).
+// Two round trips: (sequence length, bitmap), then every partial at once.
+// ---------------------------------------------------------------------------
+constexpr int kCombine = 512;
+
+template <int D>
+__global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
+    constexpr int GRP = kCombine / D;          // split subsets per channel
+    constexpr int W = kCombine / 64;
+    constexpr int PER = kMaxTeams / kCombine;  // split slots per thread at most
+    constexpr int BATCH = 16;
+    __shared__ uint32_t hw_s[kMaxWords];
+    __shared__ int32_t list_s[kMaxTeams];
+    __shared__ float f_s[kMaxTeams];
+    __shared__ float redf[W];
+    __shared__ int32_t redi[W];
+    __shared__ float acc_s[GRP][D];
+    __shared__ int32_t len_s;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bh = blockIdx.x;
+    const int b = bh / p.Hq;
+    const bool dense = p.mode == kModeDense;
+    if (!dense && tid < p.words) hw_s[tid] = p.bitmaps[size_t(bh) * p.words + tid];
+    if (tid == 0) len_s = clamp_len(p.seq_lens[b], p.P * p.T);
+    __syncthreads();
+    const int K = (len_s + p.T - 1) / p.T;
+    const int nslots = (K + p.tps - 1) / p.tps;
+    const uint32_t low = (p.tps >= 32) ? 0xffffffffu : ((1u << p.tps) - 1u);
+
+    // Compact list of the slots holding this head's partials, in slot order
+    // (thread tid owns slots tid * PER ... tid * PER + PER - 1).
+    int cnt = 0;
+    bool has[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int sp = tid * PER + i;
+        bool v = sp < nslots;
+        if (v && !dense) {
+            const int t0 = sp * p.tps;
+            v = ((hw_s[t0 >> 5] >> (t0 & 31)) & low) != 0u;
+        }
+        has[i] = v;
+        cnt += v ? 1 : 0;
+    }
+    int incl = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) redi[wave] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int w = 0; w < W; ++w) {
+        if (w < wave) base += redi[w];
+        total += redi[w];
+    }
+    int pos = base + incl - cnt;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if (has[i]) list_s[pos++] = tid * PER + i;
+    __syncthreads();
+    if (total == 0) {
+        for (int c = tid; c < D; c += kCombine) p.out[size_t(bh) * D + c] = 0.0f;
+        if (tid == 0 && p.lse) p.lse[bh] = kNegInfF;
+        return;
+    }
+
+    // Partials: (max, sum) per listed slot, and the first batch of value sums,
+    // all requested before any is used.
+    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + size_t(bh) * p.P;
+    const int c = tid % D, grp = tid / D;
+    const float *pacc = p.part_acc + size_t(bh) * p.P * D + c;
+    float x[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+        const int k = grp + u * GRP;
+        x[u] = (k < total) ? pacc[size_t(list_s[k]) * D] : 0.0f;
+    }
+    float2 v[PER];
+    float mloc = kNegInfF;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = tid + i * kCombine;
+        v[i] = (k < total) ? ml[list_s[k]] : make_float2(kNegInfF, 0.0f);
+        mloc = fmaxf(mloc, v[i].x);
+    }
+    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+    if (lane == 0) redf[wave] = mloc;
+    __syncthreads();
+    float mstar = redf[0];
+    for (int w = 1; w < W; ++w) mstar = fmaxf(mstar, redf[w]);
+    __syncthreads();
+    float lpart = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = tid + i * kCombine;
+        if (k < total) {
+            const float f = expf(v[i].x - mstar);
+            f_s[k] = f;
+            lpart += f * v[i].y;
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) lpart += __shfl_xor(lpart, off, 64);
+    if (lane == 0) redf[wave] = lpart;
+    __syncthreads();
+    float l = 0.0f;
+    for (int w = 0; w < W; ++w) l += redf[w];
+
+    float a = 0.0f;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+        const int k = grp + u * GRP;
+        if (k < total) a += f_s[k] * x[u];
+    }
+    // Further batches (more than BATCH partials per channel group): all loads
+    // of a batch are issued before any is used.
+    for (int k0 = grp + BATCH * GRP; k0 < total; k0 += BATCH * GRP) {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int k = k0 + u * GRP;
+            x[u] = (k < total) ? pacc[size_t(list_s[k]) * D] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int k = k0 + u * GRP;
+            if (k < total) a += f_s[k] * x[u];
+        }
+    }
+    acc_s[grp][c] = a;
+    __syncthreads();
+    if (tid < D) {
+        float sum = 0.0f;
+        for (int gi = 0; gi < GRP; ++gi) sum += acc_s[gi][tid];
+        p.out[size_t(bh) * D + tid] = sum / l;
+        if (tid == 0 && p.lse) p.lse[bh] = mstar + logf(l);
+    }
+}
+
+}  // namespace
+
+santa_status launch_gather(const Params &p, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid(p.max_splits, p.Hkv, p.B);
+    if (p.dtype == SANTA_BF16) {
+        // Double-buffer when a wavefront has two or more 32-token chunks.
+        const int cpt = p.T >= 32 ? p.T / 32 : 1;
+        const bool prefetch = p.tps * cpt > kWaves;
+        if (p.d == 64) {
+            if (prefetch) hipLaunchKernelGGL((gather_mfma_kernel<64, true>), grid, dim3(kBlock), 0, st, p);
+            else hipLaunchKernelGGL((gather_mfma_kernel<64, false>), grid, dim3(kBlock), 0, st, p);
+        } else {
+            if (prefetch) hipLaunchKernelGGL((gather_mfma_kernel<128, true>), grid, dim3(kBlock), 0, st, p);
+            else hipLaunchKernelGGL((gather_mfma_kernel<128, false>), grid, dim3(kBlock), 0, st, p);
+        }
+    } else {
+        if (p.d == 64) hipLaunchKernelGGL((gather_f32_kernel<64>), grid, dim3(kBlock), 0, st, p);
+        else hipLaunchKernelGGL((gather_f32_kernel<128>), grid, dim3(kBlock), 0, st, p);
+    }
+    return launched();
+}
+
+santa_status launch_combine(const Params &p, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.d == 64) hipLaunchKernelGGL((combine_kernel<64>), dim3(p.B * p.Hq), dim3(kCombine), 0, st, p);
+    else hipLaunchKernelGGL((combine_kernel<128>), dim3(p.B * p.Hq), dim3(kCombine), 0, st, p);
+    return launched();
+}
+
+}  // namespace santa

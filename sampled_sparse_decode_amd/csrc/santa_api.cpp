@@ -43,14 +43,12 @@ WorkspaceLayout workspace_layout(const santa_kv &kv) {
     return w;
 }
 
-// Union teams per split-K block: enough blocks to give every compute unit
-// several, few enough that the partial results stay a small share of the
-// bytes read.
-static int32_t teams_per_split(int64_t total_teams) {
-    int64_t tps = total_teams / 2048;
-    if (tps < 1) tps = 1;
-    if (tps > kMaxTeamsPerSplit) tps = kMaxTeamsPerSplit;
-    return int32_t(tps);
+// Teams per split-K block: a power of two (so a block's teams share one
+// bitmap word) giving about 2048 team slots per block grid, at most 16.
+static int32_t teams_per_split(int64_t team_slots) {
+    int32_t tps = 1;
+    while (tps < kMaxTeamsPerSplit && int64_t(tps) * 2 * 2048 <= team_slots) tps *= 2;
+    return tps;
 }
 
 static Params base_params(const santa_kv &kv, const void *q, float *out, float *lse,
@@ -134,10 +132,8 @@ static santa_status santa_params(const santa_kv *kv, const void *q, int32_t M, f
     *p = base_params(*kv, q, out, lse, workspace);
     p->M = M;
     p->mode = kModeSanta;
-    // The union of G heads' draws has at most min(K, G * M) teams.
-    const int64_t union_max = std::min<int64_t>(p->P, int64_t(p->G) * M);
-    p->tps = teams_per_split(int64_t(p->B) * p->Hkv * union_max);
-    p->max_splits = int32_t((union_max + p->tps - 1) / p->tps);
+    p->tps = teams_per_split(int64_t(p->B) * p->Hkv * p->P);
+    p->max_splits = (p->P + p->tps - 1) / p->tps;
     return SANTA_OK;
 }
 
@@ -190,7 +186,9 @@ santa_status dense_decode_attention(const santa_kv *kv, const void *q, float *ou
     if (st != SANTA_OK) return st;
     Params p = base_params(*kv, q, out, lse, workspace);
     p.mode = kModeDense;
+    // At most 64 splits per KV head keep the combine to one batch of loads.
     p.tps = teams_per_split(int64_t(p.B) * p.Hkv * p.P);
+    while (p.tps < kMaxTeamsPerSplit && (p.P + p.tps - 1) / p.tps > 64) p.tps *= 2;
     p.max_splits = (p.P + p.tps - 1) / p.tps;
     return run_gather_combine(p, stream);
 }

@@ -114,8 +114,9 @@ def _stream():
 class KVCache:
     """A paged KV cache on the device, in the layout of include/santa.h.
 
-    k_pages, v_pages: [num_pages][Hkv][T][d] bfloat16 or float32 tensors;
-    page_table [B][max_pages_per_seq] int32; seq_lens [B] int32.
+    k_pages: [num_pages][Hkv][T][d] and v_pages: [num_pages][Hkv][d][T],
+    bfloat16 or float32; page_table [B][max_pages_per_seq] int32; seq_lens
+    [B] int32.
     """
 
     def __init__(self, k_pages, v_pages, page_table, seq_lens, num_q_heads):
@@ -126,8 +127,9 @@ class KVCache:
             raise ValueError("k_pages / v_pages must both be bfloat16 or float32")
         if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
             raise ValueError("page_table and seq_lens must be int32")
-        if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
-            raise ValueError("k_pages and v_pages must be [num_pages][Hkv][T][d]")
+        if k_pages.dim() != 4 or tuple(v_pages.shape) != (k_pages.shape[0], k_pages.shape[1],
+                                                          k_pages.shape[3], k_pages.shape[2]):
+            raise ValueError("k_pages must be [num_pages][Hkv][T][d] and v_pages [num_pages][Hkv][d][T]")
         self.k_pages, self.v_pages = k_pages, v_pages
         self.page_table, self.seq_lens = page_table, seq_lens
         self.num_q_heads = int(num_q_heads)
@@ -173,9 +175,10 @@ def make_workspace(kv, M=1):
 
 
 def santa_build_reps(kv, reps=None):
-    """Mean key per (page, KV head), rounded to the cache dtype: [num_pages][Hkv][d]."""
+    """Mean key per (sequence, team, KV head), rounded to the cache dtype: [B][P][Hkv][d]."""
     if reps is None:
-        reps = torch.zeros((kv.num_pages, kv.num_kv_heads, kv.head_dim), dtype=kv.dtype, device=kv.device)
+        reps = torch.zeros((kv.batch, kv.max_pages_per_seq, kv.num_kv_heads, kv.head_dim), dtype=kv.dtype,
+                           device=kv.device)
     d = kv.desc()
     _check("santa_build_reps", load().santa_build_reps(ctypes.byref(d), _ptr(reps), _stream()))
     return reps

@@ -124,7 +124,7 @@ def test_reps_are_exact_rounded_means():
         n = santa.team_size(lens[0], T, t)
         for c in range(d):
             exact = sum(Fraction(float(v)) for v in kd[t, 0, :n, c]) / n
-            assert reps[t, 0, c] == _fraction_round_bf16(exact)
+            assert reps[0, t, 0, c] == _fraction_round_bf16(exact)
 
 
 # --------------------------------------------------------------------------
@@ -163,7 +163,7 @@ def test_one_token_teams_give_attention_weights():
     w = wl._contiguous("t", "f32", keys, keys, q, 1, 4)
     reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, 1, "f32")
     qh = q[0, 0].astype(np.float64)
-    s = santa.rep_scores(qh, np.stack([reps[t, 0] for t in range(L)]))
+    s = santa.rep_scores(qh, np.stack([reps[0, t, 0] for t in range(L)]))
     _, _, _, p = santa.team_softmax(s)
     eye = torch.eye(L, dtype=torch.float64)
     ref = torch.nn.functional.scaled_dot_product_attention(
@@ -283,7 +283,7 @@ def test_ht_sums_unbiased_by_enumeration(M):
     reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
     qh = numerics.decode(w.q[0, 0], "f32")
     K = 5
-    s = santa.rep_scores(qh, np.stack([reps[t, 0] for t in range(K)]))
+    s = santa.rep_scores(qh, np.stack([reps[0, t, 0] for t in range(K)]))
     _, _, _, p = santa.team_softmax(s)
     teams = [kv.team(0, 0, t) for t in range(K)]
     keys, vals = kv.all_tokens(0, 0)
@@ -334,7 +334,7 @@ def test_monte_carlo_converges_and_set_size_closed_form():
     assert np.max(np.abs(Nr.mean(axis=0) / Dr.mean() - out_d)) < 10 * np.max(seN) / Dr.mean()
     # Expected number of distinct teams: sum of inclusion probabilities.
     K = santa.num_teams(int(w.seq_lens[0]), w.page_size)
-    s = santa.rep_scores(qh, np.stack([reps[t, 0] for t in range(K)]))
+    s = santa.rep_scores(qh, np.stack([reps[0, t, 0] for t in range(K)]))
     _, _, _, p = santa.team_softmax(s)
     assert abs(sizes.mean() - santa.expected_set_size(p, w.M)) < 5 * sizes.std() / math.sqrt(R)
 
