@@ -9,8 +9,10 @@ layer with M = 31 by default. Its cache is replicated R times ("layers",
 about 1 GiB in total) and the steps cycle through them, so every step reads
 HBM rather than the 256 MB last-level cache, as a real decode step does when
 it moves from one layer's cache to the next. Inputs are resident in HBM
-before timing starts. The same is timed for the dense decode kernel, and for
-the gather + combine stage alone (the kernel that moves the bytes), whose
+before timing starts. Each call is timed as GPU time per call from HIP-graph
+replays (one call per layer captured, graph replayed), with the eager-launch
+figure reported alongside. The same is timed for the dense decode kernel, and
+for the gather + combine stage alone (the kernels that move the bytes), whose
 algorithmic bytes give the roofline figure. The CPU oracle is timed on a
 bounded sample of the same workload at the end.
 
@@ -43,6 +45,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="cache copies to cycle through (0 = enough for 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate", action="store_true", help="also run plain 64 MiB device copies (counter scale)")
     return ap.parse_args()
 
 
@@ -92,7 +95,8 @@ def algorithmic_bytes(w, stats):
                 frac_head=head_reads / dense_head_reads, frac_hbm=(attend + select) / dense)
 
 
-def time_loop(fn, steps, warmup, torch):
+def time_stream(fn, steps, warmup, torch):
+    """Eager launches: HIP events around ``steps`` calls (includes host launch cost if it dominates)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -104,6 +108,49 @@ def time_loop(fn, steps, warmup, torch):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) * 1e3 / steps       # microseconds per call
+
+
+def time_graph(fn, R, steps, warmup, torch):
+    """GPU time per call: one call per layer captured in a HIP graph, replayed;
+    HIP events around the replays on the stream they run on."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(R):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            fn(i)
+    replays = max(1, steps // R)
+    for _ in range(max(1, warmup // R)):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / (replays * R), replays * R
+
+
+def recorded_traffic(workload_name):
+    """HBM bytes per launch of the gather + combine stage from the committed
+    rocprofv3 counter summary, if the kernel source is unchanged since; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    csrc = os.path.join(ROOT, "sampled_sparse_decode_amd", "csrc")
+    src = open(os.path.join(csrc, "gather.hip"), "rb").read() + open(os.path.join(csrc, "device_common.h"), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["kernel_source_sha256"]:
+        return None
+    return int(rec["read_bytes"] + rec["write_bytes"])
 
 
 def cpu_baseline(w, budget_s):
@@ -171,11 +218,23 @@ def main():
         j = i % R
         S.santa_attend_selected(layers[j], q, M, wss[j], out, lse)
 
-    santa_us = time_loop(santa_step, args.steps, args.warmup, torch)
-    dense_us = time_loop(dense_step, args.steps, args.warmup, torch)
+    # Eager (stream) timings, then HIP-graph replay timings of the same calls.
+    santa_stream_us = time_stream(santa_step, args.steps, args.warmup, torch)
+    dense_stream_us = time_stream(dense_step, args.steps, args.warmup, torch)
+    santa_us, timed_steps = time_graph(santa_step, R, args.steps, args.warmup, torch)
+    dense_us, _ = time_graph(dense_step, R, args.steps, args.warmup, torch)
     for j in range(R):
         S.santa_select_teams(layers[j], q, reps[j], M, w.seed, w.offset, wss[j])
-    attend_us = time_loop(attend_step, args.steps, args.warmup, torch)
+    torch.cuda.synchronize()
+    attend_us, _ = time_graph(attend_step, R, args.steps, args.warmup, torch)
+    if args.calibrate:
+        # Plain device copies of a known size, so rocprofv3 FETCH_SIZE / WRITE_SIZE
+        # counters can be scaled (bytes per counter unit).
+        src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     attend_gbps = ab["attend"] / (attend_us * 1e-6) / 1e9
     step_gbps = ab["step"] / (santa_us * 1e-6) / 1e9
@@ -185,7 +244,7 @@ def main():
         "value": round(santa_us, 3),
         "unit": "us/layer",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": timed_steps,
         "warmup": args.warmup,
         "ms_per_step": round(santa_us / 1e3, 6),
         "higher_is_better": False,
@@ -196,15 +255,19 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": int(w.seq_lens.max()),
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "team_size": w.page_size, "M": M, "layers_cycled": R},
-        "santa": {"us_per_layer": round(santa_us, 3), "hbm_gbps": round(step_gbps, 1),
-                  "pct_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2), "bytes": ab["step"]},
-        "dense": {"us_per_layer": round(dense_us, 3), "hbm_gbps": round(dense_gbps, 1),
-                  "pct_peak": round(100 * dense_gbps / HBM_PEAK_GBPS, 2), "bytes": ab["dense"]},
+        "timing": "HIP-graph replay of one call per layer; eager stream figures alongside",
+        "santa": {"us_per_layer": round(santa_us, 3), "us_per_layer_stream": round(santa_stream_us, 3),
+                  "hbm_gbps": round(step_gbps, 1), "pct_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
+                  "bytes": ab["step"]},
+        "dense": {"us_per_layer": round(dense_us, 3), "us_per_layer_stream": round(dense_stream_us, 3),
+                  "hbm_gbps": round(dense_gbps, 1), "pct_peak": round(100 * dense_gbps / HBM_PEAK_GBPS, 2),
+                  "bytes": ab["dense"]},
         "speedup_vs_dense": round(dense_us / santa_us, 3),
         "kv_read_fraction": {"per_query_head": round(ab["frac_head"], 4), "hbm": round(ab["frac_hbm"], 4)},
         "roofline": {"kernel": "gather+combine (santa_attend_selected)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(attend_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": recorded_traffic(args.workload),
                      "us_per_launch": round(attend_us, 3), "bytes_per_launch": ab["attend"]},
     }
     if not args.no_cpu:

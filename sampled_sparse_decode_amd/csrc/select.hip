@@ -40,31 +40,42 @@ __global__ __launch_bounds__(kBlock) void select_kernel(Params p) {
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;
     const int b = bh / p.Hq, h = bh - b * p.Hq, g = h / p.G;
-    const int L = clamp_len(p.seq_lens[b], p.P * p.T);
-    const int K = (L + p.T - 1) / p.T;
+    const KV *reps = static_cast<const KV *>(p.reps) + size_t(b) * p.P * p.Hkv * D;
 
+    // Round trip 1: sequence length, query, and (speculatively, every row is
+    // in bounds) the first representative row of this thread.
+    const int Lraw = p.seq_lens[b];
     const KV *q = static_cast<const KV *>(p.q) + size_t(bh) * D;
     for (int c = tid; c < D; c += kBlock) q_s[c] = double(to_f32(q[c]));
     for (int w = tid; w < p.words; w += kBlock) bits_s[w] = 0u;
+    uint4 raw[CH];
+    {
+        const KV *r = reps + (size_t(tid < p.P ? tid : 0) * p.Hkv + g) * D;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) raw[j] = ld16(r + j * VPC);
+    }
+    const int L = clamp_len(Lraw, p.P * p.T);
+    const int K = (L + p.T - 1) / p.T;
     __syncthreads();
 
     // 1. Representative scores s_t = q . rep_t / sqrt(d) in float64 (the
     //    representatives are indexed by logical team: no page-table lookup).
-    const KV *reps = static_cast<const KV *>(p.reps) + size_t(b) * p.P * p.Hkv * D;
+    //    Four partial sums keep the float64 FMA chains short.
     for (int t = tid; t < K; t += kBlock) {
-        const KV *r = reps + (size_t(t) * p.Hkv + g) * D;
-        uint4 raw[CH];
+        if (t != tid) {
+            const KV *r = reps + (size_t(t) * p.Hkv + g) * D;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) raw[j] = ld16(r + j * VPC);
-        double acc = 0.0;
+            for (int j = 0; j < CH; ++j) raw[j] = ld16(r + j * VPC);
+        }
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             float f[8];
             unpack(raw[j], f, KV{});
 #pragma unroll
-            for (int e = 0; e < VPC; ++e) acc = fma(double(f[e]), q_s[j * VPC + e], acc);
+            for (int e = 0; e < VPC; ++e) acc[e & 3] = fma(double(f[e]), q_s[j * VPC + e], acc[e & 3]);
         }
-        e_s[t] = acc * p.scale;
+        e_s[t] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * p.scale;
     }
     __syncthreads();
 
