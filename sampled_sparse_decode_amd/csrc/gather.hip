@@ -48,6 +48,11 @@ struct TeamList {
     int32_t slot[kMaxTeamsPerSplit];       // team slot of each kept team
     int32_t len;                           // clamped sequence length
     int32_t nteams;
+    // union-rank mode
+    uint32_t hbits[kGM][kMaxWords];        // every team bitmap word of the group's heads
+    uint32_t uword[kMaxWords];             // their union
+    int32_t upre[kMaxWords + 1];           // exclusive prefix of the union popcounts
+    int32_t team[kMaxTeamsPerSplit];
 };
 
 // Builds the block's team list in LDS with a single round trip to memory:
@@ -110,6 +115,80 @@ __device__ int load_team_list(const Params &p, TeamList &tl, int s, int g, int b
         }
         const bool drew = (tl.mask[j] >> h) & 1u;
         tl.lnw[i][h] = drew ? (dense ? 0.0f : tl.raw_lnw[j][h]) : kNegInfF;
+    }
+    __syncthreads();
+    return nt;
+}
+
+// In union-rank mode every slot below the grid width holds a fresh (max, sum)
+// pair: a head with no team in the block gets an empty one (max -inf), which
+// the combine skips.
+__device__ __forceinline__ void write_empty_partial(const Params &p, int head, int s) {
+    reinterpret_cast<float2 *>(p.part_ml)[size_t(head) * p.P + s] = make_float2(kNegInfF, 0.0f);
+}
+
+// Union-rank team list (multi-team SANTA++ blocks): block s takes the teams
+// of union ranks [s * tps, (s + 1) * tps) of the group, so every block but the
+// last gets exactly tps drawn teams. Two round trips: the group's bitmaps and
+// the sequence length, then the teams' page ids and log weights.
+__device__ int load_ranked_team_list(const Params &p, TeamList &tl, int s, int g, int b) {
+    const int tid = threadIdx.x;
+    const int G = p.G;
+    const int hbase = b * p.Hq + g * G;
+    for (int idx = tid; idx < G * p.words; idx += kBlock) {
+        const int h = idx / p.words, w = idx - h * p.words;
+        tl.hbits[h][w] = p.bitmaps[size_t(hbase + h) * p.words + w];
+    }
+    const int Lraw = p.seq_lens[b];
+    if (tid == 0) tl.len = clamp_len(Lraw, p.P * p.T);
+    __syncthreads();
+    if (tid < 64) {
+        uint32_t u = 0u;
+        if (tid < p.words)
+            for (int h = 0; h < G; ++h) u |= tl.hbits[h][tid];
+        const int cnt = __popc(u);
+        int incl = cnt;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (tid >= off) incl += y;
+        }
+        if (tid < p.words) {
+            tl.uword[tid] = u;
+            tl.upre[tid] = incl - cnt;
+        }
+        if (tid == 63) {
+            tl.upre[p.words] = incl;
+            tl.nteams = max(0, min(p.tps, incl - s * p.tps));
+        }
+    }
+    __syncthreads();
+    const int nt = tl.nteams;
+    if (nt == 0) return 0;
+    if (tid < nt) {
+        const int r = s * p.tps + tid;
+        int lo = 0, hi = p.words - 1;             // last word whose prefix is <= r
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tl.upre[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        uint32_t u = tl.uword[lo];
+        for (int k = r - tl.upre[lo]; k > 0; --k) u &= u - 1u;
+        const int bit = __ffs(u) - 1;
+        uint32_t mask = 0u;
+        for (int h = 0; h < G; ++h) mask |= ((tl.hbits[h][lo] >> bit) & 1u) << h;
+        tl.team[tid] = lo * 32 + bit;
+        tl.mask[tid] = mask;
+    }
+    __syncthreads();
+    const int i = tid / kGM, h = tid % kGM;
+    if (i < nt) {
+        const int t = tl.team[i];
+        if (h == 0) {
+            tl.page[i] = clamp_page(p.page_table[size_t(b) * p.P + t], p.num_pages);
+            tl.n[i] = min(p.T, tl.len - t * p.T);
+        }
+        const bool drew = (tl.mask[i] >> h) & 1u;
+        tl.lnw[i][h] = drew ? p.lnw[size_t(hbase + h) * p.P + t] : kNegInfF;
     }
     __syncthreads();
     return nt;
@@ -253,8 +332,8 @@ __device__ __forceinline__ void mfma_compute_chunk(const Params &p, const TeamLi
     }
 }
 
-template <int D, bool PREFETCH>
-__global__ __launch_bounds__(kBlock, PREFETCH ? 1 : 3) void gather_mfma_kernel(Params p) {
+template <int D>
+__global__ __launch_bounds__(kBlock, 3) void gather_mfma_kernel(Params p) {
     constexpr int KS = D / 32;
     constexpr int NT = D / 16;
     __shared__ TeamList tl;
@@ -279,8 +358,11 @@ __global__ __launch_bounds__(kBlock, PREFETCH ? 1 : 3) void gather_mfma_kernel(P
             *reinterpret_cast<uint4 *>(&q_lds[h][cc * 8]) = v;
         }
     }
-    const int nteams = load_team_list(p, tl, s, g, b);
-    if (nteams == 0) return;
+    const int nteams = p.ranked ? load_ranked_team_list(p, tl, s, g, b) : load_team_list(p, tl, s, g, b);
+    if (nteams == 0) {
+        if (p.ranked && tid < G) write_empty_partial(p, hbase + tid, s);
+        return;
+    }
 
     const int cpt = p.T >= 32 ? p.T / 32 : 1;
     const int nchunks = nteams * cpt;
@@ -289,29 +371,14 @@ __global__ __launch_bounds__(kBlock, PREFETCH ? 1 : 3) void gather_mfma_kernel(P
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (PREFETCH) {
-        // Two chunk buffers in turn: the next chunk's loads are in flight
-        // while the current one is on the matrix cores.
-        MfmaChunk<D> ca, cb;
-        int q = wave;
-        if (q < nchunks) mfma_load_chunk<D>(p, tl, q, cpt, g, i16, g4, ca);
-        while (q < nchunks) {
-            const int q1 = q + kWaves;
-            if (q1 < nchunks) mfma_load_chunk<D>(p, tl, q1, cpt, g, i16, g4, cb);
-            mfma_compute_chunk<D>(p, tl, q, cpt, i16, g4, q_lds, ca, m, lsum, o);
-            if (q1 >= nchunks) break;
-            const int q2 = q1 + kWaves;
-            if (q2 < nchunks) mfma_load_chunk<D>(p, tl, q2, cpt, g, i16, g4, ca);
-            mfma_compute_chunk<D>(p, tl, q1, cpt, i16, g4, q_lds, cb, m, lsum, o);
-            q = q2;
-        }
-    } else {
-        // One chunk at a time; other resident blocks cover the load latency.
-        for (int q = wave; q < nchunks; q += kWaves) {
-            MfmaChunk<D> ck;
-            mfma_load_chunk<D>(p, tl, q, cpt, g, i16, g4, ck);
-            mfma_compute_chunk<D>(p, tl, q, cpt, i16, g4, q_lds, ck, m, lsum, o);
-        }
+    // Chunk loop: a wavefront's 16 loads of a chunk (16 KiB at d = 128) are
+    // all in flight before the first use; the other resident blocks (three
+    // per CU) cover the wait. (A double-buffered variant at one block per CU
+    // measured slower at every split size tried.)
+    for (int q = wave; q < nchunks; q += kWaves) {
+        MfmaChunk<D> ck;
+        mfma_load_chunk<D>(p, tl, q, cpt, g, i16, g4, ck);
+        mfma_compute_chunk<D>(p, tl, q, cpt, i16, g4, q_lds, ck, m, lsum, o);
     }
 
     // Wavefront partials: sums over the four lane groups of a head.
@@ -349,8 +416,11 @@ __global__ __launch_bounds__(kBlock, PREFETCH ? 1 : 3) void gather_mfma_kernel(P
     float2 *part_ml = reinterpret_cast<float2 *>(p.part_ml);
     for (int idx = tid; idx < G * D; idx += kBlock) {
         const int h = idx / D, c = idx - h * D;
-        if (hm_s[h] == kNegInfF) continue;          // the head drew no team of this split
         const size_t slot = size_t(hbase + h) * p.P + s;
+        if (hm_s[h] == kNegInfF) {                  // the head drew no team of this split
+            if (p.ranked && c == 0) write_empty_partial(p, hbase + h, s);
+            continue;
+        }
         float a = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) a += fac_s[h][w] * red_o[w][h][c];
@@ -386,8 +456,11 @@ __global__ __launch_bounds__(kBlock) void gather_f32_kernel(Params p) {
         m_s[tid] = -INFINITY;
         l_s[tid] = 0.0;
     }
-    const int nteams = load_team_list(p, tl, s, g, b);
-    if (nteams == 0) return;
+    const int nteams = p.ranked ? load_ranked_team_list(p, tl, s, g, b) : load_team_list(p, tl, s, g, b);
+    if (nteams == 0) {
+        if (p.ranked && tid < G) write_empty_partial(p, hbase + tid, s);
+        return;
+    }
 
     double (*sc)[kMaxT] = reinterpret_cast<double (*)[kMaxT]>(buf);
     const int c = tid % D, part = tid / D;
@@ -461,7 +534,10 @@ __global__ __launch_bounds__(kBlock) void gather_f32_kernel(Params p) {
     for (int idx = tid; idx < G * D; idx += kBlock) {
         const int h = idx / D, cc = idx - h * D;
         const size_t slot = size_t(hbase + h) * p.P + s;
-        if (m_s[h] == -INFINITY) continue;     // the head drew no team of this split
+        if (m_s[h] == -INFINITY) {             // the head drew no team of this split
+            if (p.ranked && cc == 0) write_empty_partial(p, hbase + h, s);
+            continue;
+        }
         double a = 0.0;
         for (int pp = 0; pp < PARTS; ++pp) a += red[pp][h][cc];
         // Store relative to the float32-rounded max the partial is labelled with.
@@ -473,144 +549,142 @@ __global__ __launch_bounds__(kBlock) void gather_f32_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: one 512-thread block per (sequence, query head). The head's bitmap
+// combine: one 256-thread block per (sequence, query head). The head's bitmap
 // says which split slots hold its partials; they are merged in slot order:
 //   out = sum_s e^{m_s - m*} acc_s / sum_s e^{m_s - m*} l_s,
 //   lse = m* + log(sum_s e^{m_s - m*} l_s).
-// Two round trips: (sequence length, bitmap), then every partial at once.
+// Two round trips: (sequence length, bitmap, every slot's (max, sum)), then
+// the value sums of the slots that hold partials, as float4, all at once.
 // ---------------------------------------------------------------------------
-constexpr int kCombine = 512;
+constexpr int kCombine = 256;
 
 template <int D>
 __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
-    constexpr int GRP = kCombine / D;          // split subsets per channel
+    constexpr int Q4 = D / 4;                      // float4 quads per row
+    constexpr int SUB = kCombine / Q4;             // split subsets (8 at d = 128, 16 at d = 64)
+    constexpr int PER = kMaxTeams / kCombine;      // slots per thread at most
     constexpr int W = kCombine / 64;
-    constexpr int PER = kMaxTeams / kCombine;  // split slots per thread at most
-    constexpr int BATCH = 16;
+    constexpr int BATCH = 8;
     __shared__ uint32_t hw_s[kMaxWords];
     __shared__ int32_t list_s[kMaxTeams];
     __shared__ float f_s[kMaxTeams];
     __shared__ float redf[W];
     __shared__ int32_t redi[W];
-    __shared__ float acc_s[GRP][D];
-    __shared__ int32_t len_s;
+    __shared__ float4 acc_s[SUB][Q4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x;
     const int b = bh / p.Hq;
     const bool dense = p.mode == kModeDense;
-    if (!dense && tid < p.words) hw_s[tid] = p.bitmaps[size_t(bh) * p.words + tid];
-    if (tid == 0) len_s = clamp_len(p.seq_lens[b], p.P * p.T);
+    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + size_t(bh) * p.P;
+
+    // Round trip 1. Slot (max, sum) values are read for every slot that can
+    // exist (all inside the workspace); stale ones are ignored below.
+    const int Lraw = p.seq_lens[b];
+    if (!dense && !p.ranked && tid < p.words) hw_s[tid] = p.bitmaps[size_t(bh) * p.words + tid];
+    const int nslots_max = p.max_splits;
+    float2 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int sp = tid * PER + i;
+        v[i] = (sp < nslots_max) ? ml[sp] : make_float2(kNegInfF, 0.0f);
+    }
     __syncthreads();
-    const int K = (len_s + p.T - 1) / p.T;
+    const int L = clamp_len(Lraw, p.P * p.T);
+    const int K = (L + p.T - 1) / p.T;
     const int nslots = (K + p.tps - 1) / p.tps;
     const uint32_t low = (p.tps >= 32) ? 0xffffffffu : ((1u << p.tps) - 1u);
 
-    // Compact list of the slots holding this head's partials, in slot order
-    // (thread tid owns slots tid * PER ... tid * PER + PER - 1).
+    // Slots holding this head's partials (thread tid owns slots tid*PER ...),
+    // their running max, and their positions in the compact list.
     int cnt = 0;
+    float mloc = kNegInfF;
     bool has[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int sp = tid * PER + i;
-        bool v = sp < nslots;
-        if (v && !dense) {
-            const int t0 = sp * p.tps;
-            v = ((hw_s[t0 >> 5] >> (t0 & 31)) & low) != 0u;
+        bool hv;
+        if (p.ranked) {
+            hv = sp < nslots_max && v[i].x != kNegInfF;
+        } else {
+            hv = sp < nslots;
+            if (hv && !dense) {
+                const int t0 = sp * p.tps;
+                hv = ((hw_s[t0 >> 5] >> (t0 & 31)) & low) != 0u;
+            }
         }
-        has[i] = v;
-        cnt += v ? 1 : 0;
+        has[i] = hv;
+        cnt += hv ? 1 : 0;
+        if (hv) mloc = fmaxf(mloc, v[i].x);
     }
     int incl = cnt;
     for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(incl, off, 64);
         if (lane >= off) incl += y;
     }
+    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
     if (lane == 63) redi[wave] = incl;
+    if (lane == 0) redf[wave] = mloc;
     __syncthreads();
     int base = 0, total = 0;
+    float mstar = kNegInfF;
     for (int w = 0; w < W; ++w) {
         if (w < wave) base += redi[w];
         total += redi[w];
+        mstar = fmaxf(mstar, redf[w]);
     }
-    int pos = base + incl - cnt;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-        if (has[i]) list_s[pos++] = tid * PER + i;
-    __syncthreads();
     if (total == 0) {
         for (int c = tid; c < D; c += kCombine) p.out[size_t(bh) * D + c] = 0.0f;
         if (tid == 0 && p.lse) p.lse[bh] = kNegInfF;
         return;
     }
-
-    // Partials: (max, sum) per listed slot, and the first batch of value sums,
-    // all requested before any is used.
-    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + size_t(bh) * p.P;
-    const int c = tid % D, grp = tid / D;
-    const float *pacc = p.part_acc + size_t(bh) * p.P * D + c;
-    float x[BATCH];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-        const int k = grp + u * GRP;
-        x[u] = (k < total) ? pacc[size_t(list_s[k]) * D] : 0.0f;
-    }
-    float2 v[PER];
-    float mloc = kNegInfF;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int k = tid + i * kCombine;
-        v[i] = (k < total) ? ml[list_s[k]] : make_float2(kNegInfF, 0.0f);
-        mloc = fmaxf(mloc, v[i].x);
-    }
-    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
-    if (lane == 0) redf[wave] = mloc;
-    __syncthreads();
-    float mstar = redf[0];
-    for (int w = 1; w < W; ++w) mstar = fmaxf(mstar, redf[w]);
-    __syncthreads();
+    int pos = base + incl - cnt;
     float lpart = 0.0f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int k = tid + i * kCombine;
-        if (k < total) {
-            const float f = expf(v[i].x - mstar);
-            f_s[k] = f;
-            lpart += f * v[i].y;
-        }
+        if (!has[i]) continue;
+        const float f = expf(v[i].x - mstar);
+        list_s[pos] = tid * PER + i;
+        f_s[pos] = f;
+        lpart += f * v[i].y;
+        ++pos;
     }
     for (int off = 32; off > 0; off >>= 1) lpart += __shfl_xor(lpart, off, 64);
+    __syncthreads();
     if (lane == 0) redf[wave] = lpart;
+
+    // Round trip 2: value sums, thread (quad c4, subset sb) takes list
+    // entries sb, sb + SUB, ... in batches whose loads are all issued first.
+    const int c4 = tid % Q4, sb = tid / Q4;
+    const float4 *pacc = reinterpret_cast<const float4 *>(p.part_acc + size_t(bh) * p.P * D) + c4;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = sb; k0 < total; k0 += BATCH * SUB) {
+        float4 x[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int k = k0 + u * SUB;
+            x[u] = (k < total) ? pacc[size_t(list_s[k]) * Q4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int k = k0 + u * SUB;
+            const float f = (k < total) ? f_s[k] : 0.0f;
+            a.x += f * x[u].x; a.y += f * x[u].y; a.z += f * x[u].z; a.w += f * x[u].w;
+        }
+    }
+    acc_s[sb][c4] = a;
     __syncthreads();
     float l = 0.0f;
     for (int w = 0; w < W; ++w) l += redf[w];
-
-    float a = 0.0f;
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-        const int k = grp + u * GRP;
-        if (k < total) a += f_s[k] * x[u];
-    }
-    // Further batches (more than BATCH partials per channel group): all loads
-    // of a batch are issued before any is used.
-    for (int k0 = grp + BATCH * GRP; k0 < total; k0 += BATCH * GRP) {
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int k = k0 + u * GRP;
-            x[u] = (k < total) ? pacc[size_t(list_s[k]) * D] : 0.0f;
+    if (tid < Q4) {
+        float4 sum = acc_s[0][tid];
+        for (int i = 1; i < SUB; ++i) {
+            const float4 y = acc_s[i][tid];
+            sum.x += y.x; sum.y += y.y; sum.z += y.z; sum.w += y.w;
         }
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int k = k0 + u * GRP;
-            if (k < total) a += f_s[k] * x[u];
-        }
-    }
-    acc_s[grp][c] = a;
-    __syncthreads();
-    if (tid < D) {
-        float sum = 0.0f;
-        for (int gi = 0; gi < GRP; ++gi) sum += acc_s[gi][tid];
-        p.out[size_t(bh) * D + tid] = sum / l;
+        const float inv = 1.0f / l;
+        reinterpret_cast<float4 *>(p.out + size_t(bh) * D)[tid] =
+            make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
         if (tid == 0 && p.lse) p.lse[bh] = mstar + logf(l);
     }
 }
@@ -621,16 +695,8 @@ santa_status launch_gather(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(p.max_splits, p.Hkv, p.B);
     if (p.dtype == SANTA_BF16) {
-        // Double-buffer when a wavefront has two or more 32-token chunks.
-        const int cpt = p.T >= 32 ? p.T / 32 : 1;
-        const bool prefetch = p.tps * cpt > kWaves;
-        if (p.d == 64) {
-            if (prefetch) hipLaunchKernelGGL((gather_mfma_kernel<64, true>), grid, dim3(kBlock), 0, st, p);
-            else hipLaunchKernelGGL((gather_mfma_kernel<64, false>), grid, dim3(kBlock), 0, st, p);
-        } else {
-            if (prefetch) hipLaunchKernelGGL((gather_mfma_kernel<128, true>), grid, dim3(kBlock), 0, st, p);
-            else hipLaunchKernelGGL((gather_mfma_kernel<128, false>), grid, dim3(kBlock), 0, st, p);
-        }
+        if (p.d == 64) hipLaunchKernelGGL((gather_mfma_kernel<64>), grid, dim3(kBlock), 0, st, p);
+        else hipLaunchKernelGGL((gather_mfma_kernel<128>), grid, dim3(kBlock), 0, st, p);
     } else {
         if (p.d == 64) hipLaunchKernelGGL((gather_f32_kernel<64>), grid, dim3(kBlock), 0, st, p);
         else hipLaunchKernelGGL((gather_f32_kernel<128>), grid, dim3(kBlock), 0, st, p);

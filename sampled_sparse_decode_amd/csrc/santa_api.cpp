@@ -44,11 +44,33 @@ WorkspaceLayout workspace_layout(const santa_kv &kv) {
 }
 
 // Teams per split-K block: a power of two (so a block's teams share one
-// bitmap word) giving about 2048 team slots per block grid, at most 16.
-static int32_t teams_per_split(int64_t team_slots) {
+// bitmap word), at most 16, giving about `target` blocks. Measured on MI355X
+// (32K and 128K contexts, batch 1-8): SANTA++ blocks, of which ~40 % find no
+// drawn team, do best near 2048 blocks; dense blocks, whose work is even, near
+// 512, with at most 128 splits per KV head.
+static int32_t teams_per_split(int64_t team_slots, int64_t target) {
     int32_t tps = 1;
-    while (tps < kMaxTeamsPerSplit && int64_t(tps) * 2 * 2048 <= team_slots) tps *= 2;
+    while (tps < kMaxTeamsPerSplit && int64_t(tps) * 2 * target <= team_slots) tps *= 2;
     return tps;
+}
+
+// SANTA++ split shape. A group (sequence, KV head) holds at most
+// U = min(P, G M) distinct drawn teams. With one team per block the blocks are
+// team ranges (one round trip before the K/V loads; blocks of undrawn teams
+// exit early). With more, blocks take tps teams by rank in the group's union,
+// so that every block but the last streams exactly tps teams.
+static void santa_split(Params *p) {
+    const int64_t groups = int64_t(p->B) * p->Hkv;
+    p->tps = teams_per_split(groups * p->P, 2048);
+    p->ranked = 0;
+    if (p->tps == 1) {
+        p->max_splits = p->P;
+        return;
+    }
+    const int64_t U = std::min<int64_t>(p->P, int64_t(p->G) * p->M);
+    p->ranked = 1;
+    p->tps = teams_per_split(groups * U, 1024);
+    p->max_splits = int32_t((U + p->tps - 1) / p->tps);
 }
 
 static Params base_params(const santa_kv &kv, const void *q, float *out, float *lse,
@@ -132,8 +154,7 @@ static santa_status santa_params(const santa_kv *kv, const void *q, int32_t M, f
     *p = base_params(*kv, q, out, lse, workspace);
     p->M = M;
     p->mode = kModeSanta;
-    p->tps = teams_per_split(int64_t(p->B) * p->Hkv * p->P);
-    p->max_splits = (p->P + p->tps - 1) / p->tps;
+    santa_split(p);
     return SANTA_OK;
 }
 
@@ -186,9 +207,8 @@ santa_status dense_decode_attention(const santa_kv *kv, const void *q, float *ou
     if (st != SANTA_OK) return st;
     Params p = base_params(*kv, q, out, lse, workspace);
     p.mode = kModeDense;
-    // At most 64 splits per KV head keep the combine to one batch of loads.
-    p.tps = teams_per_split(int64_t(p.B) * p.Hkv * p.P);
-    while (p.tps < kMaxTeamsPerSplit && (p.P + p.tps - 1) / p.tps > 64) p.tps *= 2;
+    p.tps = teams_per_split(int64_t(p.B) * p.Hkv * p.P, 512);
+    while (p.tps < kMaxTeamsPerSplit && (p.P + p.tps - 1) / p.tps > 128) p.tps *= 2;
     p.max_splits = (p.P + p.tps - 1) / p.tps;
     return run_gather_combine(p, stream);
 }

@@ -45,6 +45,7 @@ struct Params {
     int32_t mode;           // Mode
     int32_t tps;            // union teams per split-K block
     int32_t max_splits;     // gather grid.x
+    int32_t ranked;         // 1: block s takes union ranks [s*tps, (s+1)*tps); 0: team range
     double scale;           // 1 / sqrt(d)
     uint32_t *bitmaps;
     float *lnw;

@@ -23,144 +23,188 @@ namespace {
 
 using namespace dev;
 
-// One 256-thread block per (sequence b, query head h). Writes the head's team
-// bitmap and, for every drawn team t, log w_t = -log(pi_t) (0 under full
-// coverage), plus the optional sorted team list and 1/pi.
-template <typename KV, int D>
-__global__ __launch_bounds__(kBlock) void select_kernel(Params p) {
-    constexpr int VPC = KVTraits<KV>::kPerChunk;
-    constexpr int CH = D / VPC;                    // 16-byte chunks per representative row
-    __shared__ double q_s[D];
-    __shared__ double e_s[kMaxTeams];              // scores, then exp(s - max)
-    __shared__ double c_s[kMaxTeams];              // inclusive cumulative sums of e
-    __shared__ uint32_t bits_s[kMaxWords];
-    __shared__ int32_t wpre_s[kMaxWords];
-    __shared__ double red_s[kWaves];
+// One 1024-thread block per (sequence b, query head h) (16 wavefronts, four
+// per SIMD, so the float64 chains of one wavefront hide behind the others).
+// Writes the head's team bitmap and, for every drawn team t,
+// log w_t = -log(pi_t) (0 under full coverage), plus the optional sorted team
+// list and 1/pi.
+constexpr int kSel = 1024;
+constexpr int kSelWaves = kSel / 64;
+constexpr int kParts = 4;                          // threads per representative row
 
-    const int tid = threadIdx.x;
+template <typename KV, int D>
+__global__ __launch_bounds__(kSel) void select_kernel(Params p) {
+    constexpr int VPC = KVTraits<KV>::kPerChunk;
+    constexpr int CPP = D / VPC / kParts;          // 16-byte chunks per thread and row
+    constexpr int ROWS = kSel / kParts;            // rows scored per pass
+    __shared__ double q_s[D];
+    __shared__ double e_s[kMaxTeams];              // scores, then exp(s - m)
+    __shared__ double c_s[kMaxTeams];              // inclusive cumulative sums of e
+    __shared__ float lnw_s[kMaxTeams];             // log weight of each team if drawn
+    __shared__ float w_s[kMaxTeams];               // 1 / pi of each team if drawn
+    __shared__ uint32_t bits_s[kMaxWords];
+    __shared__ int32_t wpre_s[kMaxWords + 1];
+    __shared__ double redd[kSelWaves];
+    __shared__ float redf[kSelWaves];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x;
     const int b = bh / p.Hq, h = bh - b * p.Hq, g = h / p.G;
     const KV *reps = static_cast<const KV *>(p.reps) + size_t(b) * p.P * p.Hkv * D;
+    const int row0 = tid / kParts, part = tid % kParts;
 
     // Round trip 1: sequence length, query, and (speculatively, every row is
-    // in bounds) the first representative row of this thread.
+    // in bounds) this thread's quarter of representative row row0.
     const int Lraw = p.seq_lens[b];
     const KV *q = static_cast<const KV *>(p.q) + size_t(bh) * D;
-    for (int c = tid; c < D; c += kBlock) q_s[c] = double(to_f32(q[c]));
-    for (int w = tid; w < p.words; w += kBlock) bits_s[w] = 0u;
-    uint4 raw[CH];
+    if (tid < D) q_s[tid] = double(to_f32(q[tid]));
+    if (tid < p.words) bits_s[tid] = 0u;
+    uint4 raw[CPP];
     {
-        const KV *r = reps + (size_t(tid < p.P ? tid : 0) * p.Hkv + g) * D;
+        const KV *r = reps + (size_t(row0 < p.P ? row0 : 0) * p.Hkv + g) * D + part * CPP * VPC;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) raw[j] = ld16(r + j * VPC);
+        for (int j = 0; j < CPP; ++j) raw[j] = ld16(r + j * VPC);
     }
     const int L = clamp_len(Lraw, p.P * p.T);
     const int K = (L + p.T - 1) / p.T;
     __syncthreads();
 
-    // 1. Representative scores s_t = q . rep_t / sqrt(d) in float64 (the
-    //    representatives are indexed by logical team: no page-table lookup).
-    //    Four partial sums keep the float64 FMA chains short.
-    for (int t = tid; t < K; t += kBlock) {
-        if (t != tid) {
-            const KV *r = reps + (size_t(t) * p.Hkv + g) * D;
+    // 1. Representative scores s_t = q . rep_t / sqrt(d) in float64 (products
+    //    of two bfloat16 or two float32 values are exact in float64); four
+    //    threads per row, two partial sums each, added in a fixed order.
+    for (int t = row0; t < ((K + ROWS - 1) / ROWS) * ROWS; t += ROWS) {
+        if (t != row0) {
+            const KV *r = reps + (size_t(t < K ? t : 0) * p.Hkv + g) * D + part * CPP * VPC;
 #pragma unroll
-            for (int j = 0; j < CH; ++j) raw[j] = ld16(r + j * VPC);
+            for (int j = 0; j < CPP; ++j) raw[j] = ld16(r + j * VPC);
         }
-        double acc[4] = {0.0, 0.0, 0.0, 0.0};
+        double a0 = 0.0, a1 = 0.0;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
+        for (int j = 0; j < CPP; ++j) {
             float f[8];
             unpack(raw[j], f, KV{});
+            const int c0 = part * CPP * VPC + j * VPC;
 #pragma unroll
-            for (int e = 0; e < VPC; ++e) acc[e & 3] = fma(double(f[e]), q_s[j * VPC + e], acc[e & 3]);
+            for (int e = 0; e < VPC; e += 2) {
+                a0 = fma(double(f[e]), q_s[c0 + e], a0);
+                a1 = fma(double(f[e + 1]), q_s[c0 + e + 1], a1);
+            }
         }
-        e_s[t] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * p.scale;
+        double acc = a0 + a1;
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        if (part == 0 && t < K) e_s[t] = acc * p.scale;
     }
     __syncthreads();
 
-    // 2. Team softmax numerators e_t = exp(s_t - max s) and cumulative sums.
-    double m = -INFINITY;
-    for (int t = tid; t < K; t += kBlock) m = fmax(m, e_s[t]);
-    m = block_max(m, red_s);
-    for (int t = tid; t < K; t += kBlock) e_s[t] = exp(e_s[t] - m);
+    // 2. Team softmax numerators e_t = exp(s_t - m) and their cumulative sums
+    //    C_t, in float64. The shift m is the float32-rounded max: any shift at
+    //    or near the max cancels in C_t / C_last and in p_t = e_t / C_last.
+    //    Thread tid owns the contiguous teams [t0, t1).
+    float mf = -INFINITY;
+    for (int t = tid; t < K; t += kSel) mf = fmaxf(mf, float(e_s[t]));
+    for (int off = 32; off > 0; off >>= 1) mf = fmaxf(mf, __shfl_xor(mf, off, 64));
+    if (lane == 0) redf[wave] = mf;
     __syncthreads();
-    const int per = (K + kBlock - 1) / kBlock;
+    float mmax = redf[0];
+    for (int i = 1; i < kSelWaves; ++i) mmax = fmaxf(mmax, redf[i]);
+    const double m = double(mmax);
+    const int per = (K + kSel - 1) / kSel;
     const int t0 = min(K, tid * per), t1 = min(K, t0 + per);
     double local = 0.0;
-    for (int t = t0; t < t1; ++t) local += e_s[t];
-    double run = block_exclusive_sum(local, red_s);
+    for (int t = t0; t < t1; ++t) {
+        const double e = exp(e_s[t] - m);
+        e_s[t] = e;
+        local += e;
+    }
+    double incl = local;
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) redd[wave] = incl;
+    __syncthreads();
+    double base = 0.0;
+    for (int i = 0; i < wave; ++i) base += redd[i];
+    double run = base + incl - local;
     for (int t = t0; t < t1; ++t) {
         run += e_s[t];
         c_s[t] = run;
     }
     __syncthreads();
-
     const bool full = K > 0 && p.M >= K;
-    if (K > 0) {
-        const double Z = c_s[K - 1];
-        if (full) {
-            for (int t = tid; t < K; t += kBlock) atomicOr(&bits_s[t >> 5], 1u << (t & 31));
-        } else {
-            // 3. M draws with replacement: u = (x + 1/2) 2^-32 from Philox word
-            //    j mod 4 of counter (j / 4, h, b, offset); team = first t with
-            //    u Z < C_t.
-            for (int j = tid; j < p.M; j += kBlock) {
-                const uint4 r = philox4x32_10(make_uint4(uint32_t(j) >> 2, uint32_t(h), uint32_t(b), p.offset),
-                                              p.seed_lo, p.seed_hi);
-                const uint32_t x = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
-                const double u = (double(x) + 0.5) * 0x1p-32;
-                const double target = u * Z;
-                int t;
-                if (target < c_s[K - 1]) {
-                    int lo = 0, hi = K - 1;
-                    while (lo < hi) {
-                        const int mid = (lo + hi) >> 1;
-                        if (target < c_s[mid]) hi = mid; else lo = mid + 1;
-                    }
-                    t = lo;
-                } else {            // unreachable for u < 1: last team with mass
-                    t = K - 1;
-                    while (t > 0 && !(e_s[t] > 0.0)) --t;
-                }
-                atomicOr(&bits_s[t >> 5], 1u << (t & 31));
-            }
-        }
-        __syncthreads();
+    const double Z = K > 0 ? c_s[K - 1] : 0.0;
 
-        // 4. pi_t = 1 - (1 - p_t)^M, written -expm1(M log1p(-p_t)); log w_t = -log pi_t.
-        if (p.sampled) {
-            for (int w = tid; w < p.words; w += kBlock) {
-                int s = 0;
-                for (int i = 0; i < w; ++i) s += __popc(bits_s[i]);
-                wpre_s[w] = s;
+    // 3. Wavefront 0 draws; the other wavefronts compute pi_t and log w_t for
+    //    every team meanwhile (pi = 1 - (1 - p)^M = -expm1(M log1p(-p))).
+    if (K > 0) {
+        if (wave == 0) {
+            if (full) {
+                for (int t = lane; t < K; t += 64) atomicOr(&bits_s[t >> 5], 1u << (t & 31));
+            } else {
+                // M draws with replacement: u = (x + 1/2) 2^-32 from Philox word
+                // j mod 4 of counter (j / 4, h, b, offset); team = first t with
+                // u Z < C_t.
+                for (int j = lane; j < p.M; j += 64) {
+                    const uint4 r = philox4x32_10(make_uint4(uint32_t(j) >> 2, uint32_t(h), uint32_t(b), p.offset),
+                                                  p.seed_lo, p.seed_hi);
+                    const uint32_t x = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
+                    const double u = (double(x) + 0.5) * 0x1p-32;
+                    const double target = u * Z;
+                    int t;
+                    if (target < c_s[K - 1]) {
+                        int lo = 0, hi = K - 1;
+                        while (lo < hi) {
+                            const int mid = (lo + hi) >> 1;
+                            if (target < c_s[mid]) hi = mid; else lo = mid + 1;
+                        }
+                        t = lo;
+                    } else {        // unreachable for u < 1: last team with mass
+                        t = K - 1;
+                        while (t > 0 && !(e_s[t] > 0.0)) --t;
+                    }
+                    atomicOr(&bits_s[t >> 5], 1u << (t & 31));
+                }
             }
-            __syncthreads();
-        }
-        float *lnw = p.lnw + size_t(bh) * p.P;
-        for (int t = tid; t < K; t += kBlock) {
-            const uint32_t word = bits_s[t >> 5];
-            if (!((word >> (t & 31)) & 1u)) continue;
-            double lw = 0.0, w = 1.0;
-            if (!full) {
-                const double pt_ = e_s[t] / Z;
-                const double pi = -expm1(double(p.M) * log1p(-pt_));
-                w = 1.0 / pi;
-                lw = -log(pi);
-            }
-            lnw[t] = float(lw);
-            if (p.sampled) {
-                const int rank = wpre_s[t >> 5] + __popc(word & ((1u << (t & 31)) - 1u));
-                p.sampled[size_t(bh) * p.M + rank] = t;
-                p.inv_pi[size_t(bh) * p.M + rank] = float(w);
+        } else {
+            for (int t = tid - 64; t < K; t += kSel - 64) {
+                double lw = 0.0, w = 1.0;
+                if (!full) {
+                    const double pt_ = e_s[t] / Z;
+                    const double pi = -expm1(double(p.M) * log1p(-pt_));
+                    w = 1.0 / pi;
+                    lw = -log(pi);
+                }
+                lnw_s[t] = float(lw);
+                w_s[t] = float(w);
             }
         }
     }
-    for (int w = tid; w < p.words; w += kBlock) p.bitmaps[size_t(bh) * p.words + w] = bits_s[w];
+    __syncthreads();
+
+    // 4. Outputs: bitmap, log weights of drawn teams, optional sorted list.
+    if (tid < p.words) p.bitmaps[size_t(bh) * p.words + tid] = bits_s[tid];
+    if (tid == 0) {
+        int acc = 0;
+        for (int i = 0; i < p.words; ++i) {
+            wpre_s[i] = acc;
+            acc += __popc(bits_s[i]);
+        }
+        wpre_s[p.words] = acc;
+    }
+    float *lnw = p.lnw + size_t(bh) * p.P;
+    for (int t = tid; t < K; t += kSel)
+        if ((bits_s[t >> 5] >> (t & 31)) & 1u) lnw[t] = lnw_s[t];
     if (p.sampled) {
-        int total = 0;
-        for (int i = 0; i < p.words; ++i) total += __popc(bits_s[i]);
-        for (int r = total + tid; r < p.M; r += kBlock) {
+        __syncthreads();
+        for (int t = tid; t < K; t += kSel) {
+            const uint32_t word = bits_s[t >> 5];
+            if (!((word >> (t & 31)) & 1u)) continue;
+            const int rank = wpre_s[t >> 5] + __popc(word & ((1u << (t & 31)) - 1u));
+            p.sampled[size_t(bh) * p.M + rank] = t;
+            p.inv_pi[size_t(bh) * p.M + rank] = w_s[t];
+        }
+        for (int r = wpre_s[p.words] + tid; r < p.M; r += kSel) {
             p.sampled[size_t(bh) * p.M + r] = -1;
             p.inv_pi[size_t(bh) * p.M + r] = 0.0f;
         }
@@ -193,11 +237,11 @@ santa_status launch_select(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(p.B * p.Hq);
     if (p.dtype == SANTA_BF16) {
-        if (p.d == 64) hipLaunchKernelGGL((select_kernel<bf16_t, 64>), grid, dim3(kBlock), 0, st, p);
-        else hipLaunchKernelGGL((select_kernel<bf16_t, 128>), grid, dim3(kBlock), 0, st, p);
+        if (p.d == 64) hipLaunchKernelGGL((select_kernel<bf16_t, 64>), grid, dim3(kSel), 0, st, p);
+        else hipLaunchKernelGGL((select_kernel<bf16_t, 128>), grid, dim3(kSel), 0, st, p);
     } else {
-        if (p.d == 64) hipLaunchKernelGGL((select_kernel<float, 64>), grid, dim3(kBlock), 0, st, p);
-        else hipLaunchKernelGGL((select_kernel<float, 128>), grid, dim3(kBlock), 0, st, p);
+        if (p.d == 64) hipLaunchKernelGGL((select_kernel<float, 64>), grid, dim3(kSel), 0, st, p);
+        else hipLaunchKernelGGL((select_kernel<float, 128>), grid, dim3(kSel), 0, st, p);
     }
     return launched();
 }

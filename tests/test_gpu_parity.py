@@ -41,6 +41,13 @@ SMALL = {
                                               plants=3, dtype="f32"),
     "f32_d64_t256_g8": lambda: W.gaussian_mixture(batch=1, seq_len=5000, T=256, M=6, hq=8, hkv=1, d=64,
                                                   run_min=32, run_max=600, dtype="f32"),
+    # many (sequence, KV head) groups: multi-team split blocks in union-rank order
+    "bf16_b16_t16_union_rank": lambda: W.qwen_planted(batch=16, seq_len=4800, T=16, M=64, hq=8, hkv=2,
+                                                      d=64, plants=4),
+    "bf16_ragged12_t16_union_rank": lambda: W.paged_ragged(num_seqs=12, len_min=300, len_max=9000, T=16,
+                                                           M=40, hq=8, hkv=2, d=64),
+    "f32_b16_t16_union_rank": lambda: W.qwen_planted(batch=16, seq_len=4500, T=16, M=50, hq=8, hkv=2, d=64,
+                                                     plants=4, dtype="f32"),
 }
 
 
