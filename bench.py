@@ -192,7 +192,7 @@ def main():
     layers = [kv0]
     for _ in range(R - 1):
         layers.append(S.KVCache(kv0.k_pages.clone(), kv0.v_pages.clone(), kv0.page_table, kv0.seq_lens,
-                                w.num_q_heads))
+                                w.num_q_heads, w.page_size))
     reps = [S.santa_build_reps(kv) for kv in layers]
     M = w.M
     wss = [S.make_workspace(kv, M) for kv in layers]

@@ -39,12 +39,22 @@
  *
  * Paged KV layout (all entry points)
  * ----------------------------------
- *   k_pages           [num_pages][num_kv_heads][page_size][head_dim], dtype
- *                     (token-major within a page)
- *   v_pages           [num_pages][num_kv_heads][head_dim][page_size], dtype
- *                     (channel-major within a page, the value layout of
- *                     paged-attention caches: lets the matrix cores take the
- *                     P V operand straight from HBM)
+ *   k_pages, v_pages  [num_pages][num_kv_heads][tile], dtype; a tile holds
+ *                     the page_size * head_dim keys (values) of one page and
+ *                     KV head in the chunked order below
+ *   tile order        chunks of C = min(page_size, 32) tokens, C * head_dim
+ *                     elements each, in token order. Inside chunk c (tokens
+ *                     c*C .. c*C + C - 1):
+ *                       keys:   head_dim / 32 slabs, slab s = [C][32]: key of
+ *                               token c*C + i, channel 32 s + j at element
+ *                               c*C*d + s*C*32 + i*32 + j
+ *                       values: channel-major [d][C]: value of token c*C + i,
+ *                               channel ch at element c*C*d + ch*C + i
+ *                     (d = head_dim). With this order every 16-byte load of
+ *                     the decode kernels' matrix-core operands lies in a run
+ *                     of whole 128-byte lines that one instruction reads
+ *                     entirely. santa_pack_pages writes pages in this order
+ *                     from plain [page][KV head][token][channel] arrays.
  *   page_table        [batch][max_pages_per_seq] int32: physical page of
  *                     logical team t of sequence b
  *   seq_lens          [batch] int32: cached tokens L_b of sequence b
@@ -92,8 +102,8 @@ typedef struct santa_kv {
     int32_t max_pages_per_seq;  /* row length of page_table                          */
     int32_t reserved;           /* must be 0                                         */
     int64_t num_pages;          /* physical pages in k_pages / v_pages               */
-    const void *k_pages;        /* [num_pages][Hkv][T][d] dtype                      */
-    const void *v_pages;        /* [num_pages][Hkv][d][T] dtype                      */
+    const void *k_pages;        /* [num_pages][Hkv][T * d] dtype, tile order          */
+    const void *v_pages;        /* [num_pages][Hkv][T * d] dtype, tile order          */
     const int32_t *page_table;  /* [B][max_pages_per_seq]                            */
     const int32_t *seq_lens;    /* [B], each in [0, T * max_pages_per_seq]           */
 } santa_kv;
@@ -184,6 +194,20 @@ santa_status santa_attention_given_teams(const santa_kv *kv, const void *q, int3
                                          const int32_t *teams, const float *weights,
                                          float *out, float *lse,
                                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Writes whole pages into the cache's tile order (a pure permutation; every
+ * element is copied bit for bit). Not a step of the method: it is how a
+ * caller lays out pages after prefill or after filling a page.
+ *   k_src, v_src  [num_pages][num_kv_heads][page_size][head_dim] dtype
+ *   k_dst, v_dst  [num_pages][num_kv_heads][page_size * head_dim] dtype, in
+ *                 the tile order of "Paged KV layout" above
+ * dtype, page_size and head_dim as for santa_kv; num_kv_heads >= 1;
+ * num_pages >= 0 (0 enqueues nothing); num_pages * num_kv_heads < 2^31. The
+ * four buffers must not overlap (SANTA_ERR_SHAPE if their byte ranges do). */
+santa_status santa_pack_pages(int32_t dtype, int64_t num_pages, int32_t num_kv_heads,
+                              int32_t page_size, int32_t head_dim,
+                              const void *k_src, const void *v_src, void *k_dst, void *v_dst,
+                              void *stream);
 
 /* Static description of a status code. */
 const char *santa_status_string(int32_t status);

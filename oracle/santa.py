@@ -265,11 +265,10 @@ def dense_attention(q_h, keys, vals):
 # ----------------------------------------------------------------------------
 
 class PagedKV:
-    """Float64 view of a paged KV cache as the library lays it out.
+    """Float64 view of a paged KV cache (pages in plain token-major order).
 
-    k_pages: stored array [num_pages][Hkv][T][d] (uint16 bf16 bits or
-    float32), token-major; v_pages: [num_pages][Hkv][d][T], channel-major
-    within a page; page_table [B][max_pages]; seq_lens [B]. Pages are decoded
+    k_pages, v_pages: stored arrays [num_pages][Hkv][T][d] (uint16 bf16 bits
+    or float32); page_table [B][max_pages]; seq_lens [B]. Pages are decoded
     to float64 on first use.
     """
 
@@ -292,7 +291,7 @@ class PagedKV:
         p = int(self.page_table[b][t])
         n = team_size(L, self.T, t)
         return (self._page(self._k, self.k_raw, p)[g, :n, :],
-                self._page(self._v, self.v_raw, p)[g, :, :n].T)
+                self._page(self._v, self.v_raw, p)[g, :n, :])
 
     def all_tokens(self, b, g):
         L = int(self.seq_lens[b])

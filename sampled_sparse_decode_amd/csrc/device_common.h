@@ -69,6 +69,21 @@ __device__ __forceinline__ bf16_t f64_to_bf16(double x) {
 __device__ __forceinline__ void store_rounded(bf16_t *dst, double x) { *dst = f64_to_bf16(x); }
 __device__ __forceinline__ void store_rounded(float *dst, double x) { *dst = float(x); }   // IEEE RNE
 
+// Page tile layout of the cache (one tile per (page, KV head), T * d elements).
+// A tile is cut into chunks of C = min(T, 32) tokens, C * d elements each.
+// Inside a chunk, keys are stored as d / 32 slabs of [C tokens][32 channels]
+// and values channel-major as [d][C tokens]. Both offsets are in elements
+// from the start of the tile.
+__host__ __device__ __forceinline__ int chunk_tokens(int T) { return T < 32 ? T : 32; }
+__host__ __device__ __forceinline__ int k_offset(int tok, int ch, int T, int d) {
+    const int C = chunk_tokens(T);
+    return (tok / C) * (C * d) + (ch >> 5) * (C * 32) + (tok % C) * 32 + (ch & 31);
+}
+__host__ __device__ __forceinline__ int v_offset(int tok, int ch, int T, int d) {
+    const int C = chunk_tokens(T);
+    return (tok / C) * (C * d) + ch * C + tok % C;
+}
+
 __device__ __forceinline__ int clamp_len(int L, int max_len) {
     return L < 0 ? 0 : (L > max_len ? max_len : L);
 }

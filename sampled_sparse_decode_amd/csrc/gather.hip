@@ -24,9 +24,11 @@
 // merges them in split order. Blocks whose teams nobody drew exit after the
 // first round trip.
 //
-// Cache layout: K pages [page][g][T][d] (token-major), V pages [page][g][d][T]
-// (channel-major within a page), so that both matrix-core operands of the
-// bf16 path are plain 16-byte loads from HBM.
+// Cache layout: each (page, KV head) tile is cut into chunks of 32 tokens;
+// keys are stored as 32-channel slabs [32 tokens][32 channels] and values
+// channel-major [d][32 tokens] inside a chunk. Every 16-byte load of a
+// matrix-core operand then sits in a run of whole 128-byte lines that the
+// same instruction reads completely.
 #include "device_common.h"
 
 namespace santa {
@@ -219,26 +221,35 @@ struct MfmaChunk {
 // valid row (K; those scores are masked) or to its first 8 tokens (V; zeroed
 // by keep_first), so every address stays inside the page and the wavefront
 // issues all of its loads back to back.
+// Chunk (tokens tb .. tb + 31 of a team with n valid tokens; C = min(T, 32)
+// of them stored): K slab ks holds [C][32] elements, V is [D][C]. For a tile
+// of 16 keys the four 64-byte runs of a slab that one instruction reads are
+// whole lines.
+template <int D>
+__device__ __forceinline__ void mfma_load_chunk_at(const Params &p, int64_t page, int n, int tb, int g,
+                                                   int i16, int g4, MfmaChunk<D> &c) {
+    const int C = chunk_tokens(p.T);
+    const size_t base = (size_t(page) * p.Hkv + g) * size_t(p.T) * D + size_t(tb) * D;
+    const bf16_t *kc = static_cast<const bf16_t *>(p.k_pages) + base;
+    const bf16_t *vc = static_cast<const bf16_t *>(p.v_pages) + base;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int tok = 8 * (i16 >> 2) + 4 * t + (i16 & 3);     // in-chunk token of this lane's row
+        const bf16_t *row = kc + min(tok, max(n - 1 - tb, 0)) * 32 + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < MfmaChunk<D>::KS; ++ks) c.k[t][ks] = ld16(row + ks * (C * 32));
+    }
+    const int tok0 = 8 * g4;
+    const bf16_t *col = vc + i16 * C + (tb + tok0 < n ? tok0 : 0);
+#pragma unroll
+    for (int nt = 0; nt < MfmaChunk<D>::NT; ++nt) c.v[nt] = ld16(col + (16 * nt) * C);
+}
+
 template <int D>
 __device__ __forceinline__ void mfma_load_chunk(const Params &p, const TeamList &tl, int q, int cpt, int g,
                                                 int i16, int g4, MfmaChunk<D> &c) {
     const int ti = q / cpt;
-    const int tb = (q - ti * cpt) * 32;
-    const int n = tl.n[ti];
-    const size_t tile = (size_t(tl.page[ti]) * p.Hkv + g) * size_t(p.T) * D;
-    const bf16_t *kt = static_cast<const bf16_t *>(p.k_pages) + tile;
-    const bf16_t *vt = static_cast<const bf16_t *>(p.v_pages) + tile;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int tok = tb + 8 * (i16 >> 2) + 4 * t + (i16 & 3);
-        const bf16_t *row = kt + size_t(min(tok, n - 1)) * D + 8 * g4;
-#pragma unroll
-        for (int ks = 0; ks < MfmaChunk<D>::KS; ++ks) c.k[t][ks] = ld16(row + 32 * ks);
-    }
-    const int tok0 = tb + 8 * g4;
-    const bf16_t *col = vt + size_t(i16) * p.T + (tok0 < n ? tok0 : 0);
-#pragma unroll
-    for (int nt = 0; nt < MfmaChunk<D>::NT; ++nt) c.v[nt] = ld16(col + size_t(16 * nt) * p.T);
+    mfma_load_chunk_at<D>(p, tl.page[ti], tl.n[ti], (q - ti * cpt) * 32, g, i16, g4, c);
 }
 
 // Zero the bf16 elements e >= keep of a 16-byte operand (ragged team tails).
@@ -255,15 +266,13 @@ __device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Scores, online-softmax update and P V for one chunk; lw is the log weight
+// of head i16 for the chunk's team (-inf: the head did not draw it).
 template <int D>
-__device__ __forceinline__ void mfma_compute_chunk(const Params &p, const TeamList &tl, int q, int cpt,
-                                                   int i16, int g4, const bf16_t (*q_lds)[D + 8],
-                                                   const MfmaChunk<D> &c, float &m, float &lsum,
-                                                   f32x4 (&o)[D / 16]) {
-    const int ti = q / cpt;
-    const int tb = (q - ti * cpt) * 32;
-    const int n = tl.n[ti];
-    const float lw = tl.lnw[ti][i16];
+__device__ __forceinline__ void mfma_compute_chunk_at(const Params &p, int n, int tb, float lw,
+                                                      int i16, int g4, const bf16_t (*q_lds)[D + 8],
+                                                      const MfmaChunk<D> &c, float &m, float &lsum,
+                                                      f32x4 (&o)[D / 16]) {
     const float scale = float(p.scale);
 
     f32x4 st[2];
@@ -333,14 +342,104 @@ __device__ __forceinline__ void mfma_compute_chunk(const Params &p, const TeamLi
 }
 
 template <int D>
-__global__ __launch_bounds__(kBlock, 3) void gather_mfma_kernel(Params p) {
-    constexpr int KS = D / 32;
+__device__ __forceinline__ void mfma_compute_chunk(const Params &p, const TeamList &tl, int q, int cpt,
+                                                   int i16, int g4, const bf16_t (*q_lds)[D + 8],
+                                                   const MfmaChunk<D> &c, float &m, float &lsum,
+                                                   f32x4 (&o)[D / 16]) {
+    const int ti = q / cpt;
+    mfma_compute_chunk_at<D>(p, tl.n[ti], (q - ti * cpt) * 32, tl.lnw[ti][i16], i16, g4, q_lds, c, m, lsum, o);
+}
+
+// Cross-wavefront merge of the online-softmax states and the store of the
+// block's partial at slot s of every head of the group.
+template <int D>
+struct MfmaReduce {
+    float m[kWaves][kGM];
+    float l[kWaves][kGM];
+    float o[kWaves][kGM][D];
+    float fac[kGM][kWaves];
+    float hm[kGM], hl[kGM];
+};
+
+template <int D>
+__device__ __forceinline__ void mfma_store_partial(const Params &p, MfmaReduce<D> &rd, float m, float lsum,
+                                                   const f32x4 (&o)[D / 16], int hbase, int s) {
     constexpr int NT = D / 16;
-    __shared__ TeamList tl;
-    __shared__ __attribute__((aligned(16))) bf16_t q_lds[kGM][D + 8];
-    __shared__ float red_m[kWaves][kGM];
-    __shared__ float red_l[kWaves][kGM];
-    __shared__ float red_o[kWaves][kGM][D];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int G = p.G;
+    __syncthreads();                              // rd may alias the chunk loop's LDS
+    // Wavefront partials: sums over the four lane groups of a head.
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (g4 == 0) {
+        rd.m[wave][i16] = m;
+        rd.l[wave][i16] = lsum;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rd.o[wave][4 * g4 + e][16 * nt + i16] = o[nt][e];
+    __syncthreads();
+
+    // Merge the wavefronts in a fixed order; the per-(head, wavefront) scale
+    // factors are computed once.
+    if (tid < G) {
+        const int h = tid;
+        float mx = rd.m[0][h];
+        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, rd.m[w][h]);
+        float l = 0.0f;
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = (rd.m[w][h] == kNegInfF) ? 0.0f : expf(rd.m[w][h] - mx);
+            rd.fac[h][w] = f;
+            l += f * rd.l[w][h];
+        }
+        rd.hm[h] = mx;
+        rd.hl[h] = l;
+    }
+    __syncthreads();
+    float2 *part_ml = reinterpret_cast<float2 *>(p.part_ml);
+    for (int idx = tid; idx < G * D; idx += kBlock) {
+        const int h = idx / D, c = idx - h * D;
+        const size_t slot = size_t(hbase + h) * p.P + s;
+        if (rd.hm[h] == kNegInfF) {                 // no team of this block for the head
+            if (p.ranked && c == 0) write_empty_partial(p, hbase + h, s);
+            continue;
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) a += rd.fac[h][w] * rd.o[w][h][c];
+        p.part_acc[slot * D + c] = a;
+        if (c == 0) part_ml[slot] = make_float2(rd.hm[h], rd.hl[h]);
+    }
+}
+
+// Q^T operand rows (head slots >= G are zero), kept in LDS and read per
+// chunk; rows padded by 16 bytes so the 16 head rows hit different banks.
+template <int D>
+__device__ __forceinline__ void fill_q_lds(const Params &p, bf16_t (*q_lds)[D + 8], int hbase) {
+    const int tid = threadIdx.x;
+    const int h = tid >> 4, cc = tid & 15;                // 16 heads x 16 pieces of 16 bytes
+    if (cc * 8 < D) {
+        const uint4 v = (h < p.G) ? ld16(static_cast<const bf16_t *>(p.q) + size_t(hbase + h) * D + cc * 8)
+                                  : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(&q_lds[h][cc * 8]) = v;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock, 3) void gather_mfma_kernel(Params p) {
+    constexpr int NT = D / 16;
+    struct Stream {
+        TeamList tl;
+        __attribute__((aligned(16))) bf16_t q_lds[kGM][D + 8];
+    };
+    __shared__ union {
+        Stream st;
+        MfmaReduce<D> rd;                         // used once the chunk loop is done
+    } lds;
+    TeamList &tl = lds.st.tl;
+    bf16_t (*q_lds)[D + 8] = lds.st.q_lds;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -348,16 +447,7 @@ __global__ __launch_bounds__(kBlock, 3) void gather_mfma_kernel(Params p) {
     const int G = p.G;
     const int hbase = b * p.Hq + g * G;
 
-    // Q^T operand rows (head slots >= G are zero), kept in LDS and read per
-    // chunk; rows padded by 16 bytes so the 16 head rows hit different banks.
-    {
-        const int h = tid >> 4, cc = tid & 15;            // 16 heads x 16 chunks of 16 bytes
-        if (cc * 8 < D) {
-            const uint4 v = (h < G) ? ld16(static_cast<const bf16_t *>(p.q) + size_t(hbase + h) * D + cc * 8)
-                                    : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(&q_lds[h][cc * 8]) = v;
-        }
-    }
+    fill_q_lds<D>(p, q_lds, hbase);
     const int nteams = p.ranked ? load_ranked_team_list(p, tl, s, g, b) : load_team_list(p, tl, s, g, b);
     if (nteams == 0) {
         if (p.ranked && tid < G) write_empty_partial(p, hbase + tid, s);
@@ -373,60 +463,157 @@ __global__ __launch_bounds__(kBlock, 3) void gather_mfma_kernel(Params p) {
 
     // Chunk loop: a wavefront's 16 loads of a chunk (16 KiB at d = 128) are
     // all in flight before the first use; the other resident blocks (three
-    // per CU) cover the wait. (A double-buffered variant at one block per CU
-    // measured slower at every split size tried.)
+    // per CU) cover the wait.
     for (int q = wave; q < nchunks; q += kWaves) {
         MfmaChunk<D> ck;
         mfma_load_chunk<D>(p, tl, q, cpt, g, i16, g4, ck);
         mfma_compute_chunk<D>(p, tl, q, cpt, i16, g4, q_lds, ck, m, lsum, o);
     }
+    mfma_store_partial<D>(p, lds.rd, m, lsum, o, hbase, s);
+}
 
-    // Wavefront partials: sums over the four lane groups of a head.
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-    if (g4 == 0) {
-        red_m[wave][i16] = m;
-        red_l[wave][i16] = lsum;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red_o[wave][4 * g4 + e][16 * nt + i16] = o[nt][e];
-    __syncthreads();
+// ---------------------------------------------------------------------------
+// Balanced gather (bf16): the chunks of a (sequence, KV head) group are
+// listed in order, chunk c being 32-token piece (c mod cpt) of the union team
+// of rank c / cpt (union of the teams the group's query heads drew; every
+// team in dense mode), and block j of nb = gridDim.x takes the contiguous
+// range [j C / nb, (j + 1) C / nb) of the C chunks, so every block of a group
+// gets the same number of chunks to within one. Round trip 1 brings the
+// group's bitmaps and the sequence's page-table row; a chunk's log weights
+// are loaded with its K/V tiles (round trip 2), so no load waits on another
+// beyond these two. Each block merges and stores one partial per head.
+// ---------------------------------------------------------------------------
+constexpr int kWin = 64;
 
-    // Merge the wavefronts in a fixed order; one partial per head that drew a
-    // team of this split. The per-(head, wavefront) scale factors are
-    // computed once.
-    __shared__ float fac_s[kGM][kWaves];
-    __shared__ float hm_s[kGM], hl_s[kGM];
-    if (tid < G) {
-        const int h = tid;
-        float mx = red_m[0][h];
-        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, red_m[w][h]);
-        float l = 0.0f;
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = (red_m[w][h] == kNegInfF) ? 0.0f : expf(red_m[w][h] - mx);
-            fac_s[h][w] = f;
-            l += f * red_l[w][h];
+struct GroupChunks {
+    uint32_t hbits[kGM][kMaxWords];        // team bitmaps of the group's heads
+    uint32_t uword[kMaxWords];             // their union
+    int32_t upre[kMaxWords + 1];           // exclusive prefix of the union popcounts
+    int32_t len;                           // clamped sequence length
+    int32_t pt[kMaxTeams];                 // the sequence's page-table row
+    int64_t page[kWin];
+    int32_t n[kWin];                       // valid tokens of the chunk's team
+    int32_t tb[kWin];                      // first token of the chunk within its team
+    int32_t team[kWin];
+    uint32_t mask[kWin];                   // heads that drew the chunk's team
+};
+
+// Round trip 1 and the union: words, popcount prefix; returns the union size.
+__device__ int group_union(const Params &p, GroupChunks &gc, int g, int b) {
+    const int tid = threadIdx.x;
+    const int G = p.G;
+    const bool dense = p.mode == kModeDense;
+    const int hbase = b * p.Hq + g * G;
+    const int Lraw = p.seq_lens[b];
+    for (int t = tid; t < p.P; t += kBlock) gc.pt[t] = p.page_table[size_t(b) * p.P + t];
+    if (!dense)
+        for (int idx = tid; idx < G * p.words; idx += kBlock) {
+            const int h = idx / p.words, w = idx - h * p.words;
+            gc.hbits[h][w] = p.bitmaps[size_t(hbase + h) * p.words + w];
         }
-        hm_s[h] = mx;
-        hl_s[h] = l;
+    if (tid == 0) gc.len = clamp_len(Lraw, p.P * p.T);
+    __syncthreads();
+    if (tid < 64) {
+        const int K = (gc.len + p.T - 1) / p.T;
+        uint32_t u = 0u;
+        if (tid < p.words) {
+            if (dense) {
+                const int lo = tid * 32;
+                u = (K >= lo + 32) ? 0xffffffffu : (K > lo ? ((1u << (K - lo)) - 1u) : 0u);
+            } else {
+                for (int h = 0; h < G; ++h) u |= gc.hbits[h][tid];
+            }
+        }
+        const int cnt = __popc(u);
+        int incl = cnt;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (tid >= off) incl += y;
+        }
+        if (tid < p.words) {
+            gc.uword[tid] = u;
+            gc.upre[tid] = incl - cnt;
+        }
+        if (tid == 63) gc.upre[p.words] = incl;
     }
     __syncthreads();
-    float2 *part_ml = reinterpret_cast<float2 *>(p.part_ml);
-    for (int idx = tid; idx < G * D; idx += kBlock) {
-        const int h = idx / D, c = idx - h * D;
-        const size_t slot = size_t(hbase + h) * p.P + s;
-        if (hm_s[h] == kNegInfF) {                  // the head drew no team of this split
-            if (p.ranked && c == 0) write_empty_partial(p, hbase + h, s);
-            continue;
+    return gc.upre[p.words];
+}
+
+// Chunks c0 .. c0 + cnt - 1 (cnt <= kWin) of the group: team, heads, page,
+// size, from LDS only.
+__device__ void chunk_window(const Params &p, GroupChunks &gc, int cpt, int c0, int cnt) {
+    const int tid = threadIdx.x;
+    const int G = p.G;
+    if (tid < cnt) {
+        const int ci = c0 + tid;
+        const int r = ci / cpt, c = ci - r * cpt;
+        int lo = 0, hi = p.words - 1;             // last word whose prefix is <= r
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (gc.upre[mid] <= r) lo = mid; else hi = mid - 1;
         }
-        float a = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) a += fac_s[h][w] * red_o[w][h][c];
-        p.part_acc[slot * D + c] = a;
-        if (c == 0) part_ml[slot] = make_float2(hm_s[h], hl_s[h]);
+        uint32_t u = gc.uword[lo];
+        for (int k = r - gc.upre[lo]; k > 0; --k) u &= u - 1u;
+        const int bit = __ffs(u) - 1;
+        const int t = lo * 32 + bit;
+        uint32_t mask = 0u;
+        if (p.mode == kModeDense) mask = (1u << G) - 1u;
+        else
+            for (int h = 0; h < G; ++h) mask |= ((gc.hbits[h][lo] >> bit) & 1u) << h;
+        gc.team[tid] = t;
+        gc.mask[tid] = mask;
+        gc.tb[tid] = c * 32;
+        gc.page[tid] = clamp_page(gc.pt[t], p.num_pages);
+        gc.n[tid] = min(p.T, gc.len - t * p.T);
     }
+    __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock, 3) void gather_balanced_kernel(Params p) {
+    constexpr int NT = D / 16;
+    struct Stream {
+        GroupChunks gc;
+        __attribute__((aligned(16))) bf16_t q_lds[kGM][D + 8];
+    };
+    __shared__ union {
+        Stream st;
+        MfmaReduce<D> rd;                         // used once the chunk loop is done
+    } lds;
+    GroupChunks &gc = lds.st.gc;
+
+    const int j = blockIdx.x, nb = gridDim.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int hbase = b * p.Hq + g * p.G;
+    const bool dense = p.mode == kModeDense;
+
+    fill_q_lds<D>(p, lds.st.q_lds, hbase);
+    const int U = group_union(p, gc, g, b);
+    const int cpt = p.T >= 32 ? p.T / 32 : 1;
+    const int total = U * cpt;
+    const int c0 = int((long long)total * j / nb), c1 = int((long long)total * (j + 1) / nb);
+
+    float m = kNegInfF, lsum = 0.0f;
+    f32x4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *lnw_h = p.lnw + size_t(hbase + i16) * p.P;
+    for (int w0 = c0; w0 < c1; w0 += kWin) {
+        const int cnt = min(kWin, c1 - w0);
+        chunk_window(p, gc, cpt, w0, cnt);
+        for (int q = wave; q < cnt; q += kWaves) {
+            const bool drew = (gc.mask[q] >> i16) & 1u;
+            const float lw_raw = (drew && !dense) ? lnw_h[gc.team[q]] : 0.0f;
+            MfmaChunk<D> ck;
+            mfma_load_chunk_at<D>(p, gc.page[q], gc.n[q], gc.tb[q], g, i16, g4, ck);
+            const float lw = drew ? lw_raw : kNegInfF;
+            mfma_compute_chunk_at<D>(p, gc.n[q], gc.tb[q], lw, i16, g4, lds.st.q_lds, ck, m, lsum, o);
+        }
+        __syncthreads();                          // the window is reused
+    }
+    mfma_store_partial<D>(p, lds.rd, m, lsum, o, hbase, j);
 }
 
 // ---------------------------------------------------------------------------
@@ -482,7 +669,7 @@ __global__ __launch_bounds__(kBlock) void gather_f32_kernel(Params p) {
             }
             double dot = 0.0;
             for (int c0 = 0; c0 < D; c0 += 4) {
-                const uint4 r = ld16(kt + size_t(j) * D + c0);
+                const uint4 r = ld16(kt + k_offset(j, c0, p.T, D));
                 dot = fma(double(__uint_as_float(r.x)), double(q_s[h][c0 + 0]), dot);
                 dot = fma(double(__uint_as_float(r.y)), double(q_s[h][c0 + 1]), dot);
                 dot = fma(double(__uint_as_float(r.z)), double(q_s[h][c0 + 2]), dot);
@@ -518,7 +705,7 @@ __global__ __launch_bounds__(kBlock) void gather_f32_kernel(Params p) {
         for (int h = 0; h < kGM; ++h)
             if (h < G) acc[h] *= corr_s[h];
         for (int j = part; j < n; j += PARTS) {
-            const double v = double(vt[size_t(c) * p.T + j]);
+            const double v = double(vt[v_offset(j, c, p.T, D)]);
 #pragma unroll
             for (int h = 0; h < kGM; ++h)
                 if (h < G) acc[h] = fma(sc[h][j], v, acc[h]);
@@ -694,7 +881,10 @@ __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
 santa_status launch_gather(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(p.max_splits, p.Hkv, p.B);
-    if (p.dtype == SANTA_BF16) {
+    if (p.dtype == SANTA_BF16 && p.balanced) {
+        if (p.d == 64) hipLaunchKernelGGL((gather_balanced_kernel<64>), grid, dim3(kBlock), 0, st, p);
+        else hipLaunchKernelGGL((gather_balanced_kernel<128>), grid, dim3(kBlock), 0, st, p);
+    } else if (p.dtype == SANTA_BF16) {
         if (p.d == 64) hipLaunchKernelGGL((gather_mfma_kernel<64>), grid, dim3(kBlock), 0, st, p);
         else hipLaunchKernelGGL((gather_mfma_kernel<128>), grid, dim3(kBlock), 0, st, p);
     } else {

@@ -43,24 +43,40 @@ WorkspaceLayout workspace_layout(const santa_kv &kv) {
     return w;
 }
 
-// Teams per split-K block: a power of two (so a block's teams share one
-// bitmap word), at most 16, giving about `target` blocks. Measured on MI355X
-// (32K and 128K contexts, batch 1-8): SANTA++ blocks, of which ~40 % find no
-// drawn team, do best near 2048 blocks; dense blocks, whose work is even, near
-// 512, with at most 128 splits per KV head.
+// Teams per split-K block of the float32 path: a power of two (so a block's
+// teams share one bitmap word), at most 16, giving about `target` blocks.
 static int32_t teams_per_split(int64_t team_slots, int64_t target) {
     int32_t tps = 1;
     while (tps < kMaxTeamsPerSplit && int64_t(tps) * 2 * target <= team_slots) tps *= 2;
     return tps;
 }
 
-// SANTA++ split shape. A group (sequence, KV head) holds at most
-// U = min(P, G M) distinct drawn teams. With one team per block the blocks are
-// team ranges (one round trip before the K/V loads; blocks of undrawn teams
-// exit early). With more, blocks take tps teams by rank in the group's union,
-// so that every block but the last streams exactly tps teams.
+// Split shapes. bfloat16 caches use balanced blocks: each (sequence, KV
+// head) group gets nb blocks that split the group's chunks (32-token pieces
+// of its drawn teams, or of every team for dense) into even contiguous
+// ranges, about kBalancedBlocks blocks in all: one per CU streamed best on
+// MI355X at 32K-128K contexts, batch 1-8 (more blocks only add prologues).
+// float32 caches use team ranges (one round trip before the K/V loads;
+// blocks of undrawn teams exit early) or, with several teams per block,
+// union ranks: a group holds at most U = min(P, G M) distinct drawn teams and
+// block s takes those of ranks [s tps, (s + 1) tps).
+constexpr int64_t kBalancedBlocks = 256;
+
+static void balanced_split(Params *p) {
+    const int64_t groups = int64_t(p->B) * p->Hkv;
+    p->balanced = 1;
+    p->ranked = 1;
+    p->tps = 1;
+    p->max_splits = int32_t(std::min<int64_t>(p->P, std::max<int64_t>(1, (kBalancedBlocks + groups - 1) / groups)));
+}
+
 static void santa_split(Params *p) {
     const int64_t groups = int64_t(p->B) * p->Hkv;
+    p->balanced = 0;
+    if (p->dtype == SANTA_BF16) {
+        balanced_split(p);
+        return;
+    }
     p->tps = teams_per_split(groups * p->P, 2048);
     p->ranked = 0;
     if (p->tps == 1) {
@@ -207,9 +223,13 @@ santa_status dense_decode_attention(const santa_kv *kv, const void *q, float *ou
     if (st != SANTA_OK) return st;
     Params p = base_params(*kv, q, out, lse, workspace);
     p.mode = kModeDense;
-    p.tps = teams_per_split(int64_t(p.B) * p.Hkv * p.P, 512);
-    while (p.tps < kMaxTeamsPerSplit && (p.P + p.tps - 1) / p.tps > 128) p.tps *= 2;
-    p.max_splits = (p.P + p.tps - 1) / p.tps;
+    if (p.dtype == SANTA_BF16) {
+        balanced_split(&p);
+    } else {
+        p.tps = teams_per_split(int64_t(p.B) * p.Hkv * p.P, 512);
+        while (p.tps < kMaxTeamsPerSplit && (p.P + p.tps - 1) / p.tps > 128) p.tps *= 2;
+        p.max_splits = (p.P + p.tps - 1) / p.tps;
+    }
     return run_gather_combine(p, stream);
 }
 
@@ -228,6 +248,29 @@ santa_status santa_attention_given_teams(const santa_kv *kv, const void *q, int3
     return run_gather_combine(p, stream);
 }
 
+santa_status santa_pack_pages(int32_t dtype, int64_t num_pages, int32_t num_kv_heads,
+                              int32_t page_size, int32_t head_dim,
+                              const void *k_src, const void *v_src, void *k_dst, void *v_dst,
+                              void *stream) {
+    if (dtype != SANTA_F32 && dtype != SANTA_BF16) return SANTA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return SANTA_ERR_UNSUPPORTED;
+    const int T = page_size;
+    if (T != 16 && T != 32 && T != 64 && T != 128 && T != 256) return SANTA_ERR_UNSUPPORTED;
+    if (num_kv_heads < 1 || num_pages < 0) return SANTA_ERR_SHAPE;
+    if (num_pages > (int64_t(1) << 31) / num_kv_heads) return SANTA_ERR_SHAPE;
+    const int64_t tiles = num_pages * num_kv_heads;
+    if (tiles >= (int64_t(1) << 31)) return SANTA_ERR_SHAPE;
+    if (tiles == 0) return SANTA_OK;
+    if (!k_src || !v_src || !k_dst || !v_dst) return SANTA_ERR_NULL;
+    const uintptr_t bytes = uintptr_t(tiles) * uintptr_t(T) * uintptr_t(head_dim) * (dtype == SANTA_BF16 ? 2u : 4u);
+    const uintptr_t lo[4] = {uintptr_t(k_src), uintptr_t(v_src), uintptr_t(k_dst), uintptr_t(v_dst)};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if ((i >= 2 || j >= 2) && lo[i] < lo[j] + bytes && lo[j] < lo[i] + bytes) return SANTA_ERR_SHAPE;
+    PackParams pp{k_src, v_src, k_dst, v_dst, tiles, dtype, T, head_dim};
+    return launch_pack_pages(pp, stream);
+}
+
 const char *santa_status_string(int32_t status) {
     switch (status) {
         case SANTA_OK: return "ok";
@@ -240,6 +283,6 @@ const char *santa_status_string(int32_t status) {
     }
 }
 
-int32_t santa_version(void) { return 100; }
+int32_t santa_version(void) { return 200; }
 
 }  // extern "C"

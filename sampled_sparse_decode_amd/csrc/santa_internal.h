@@ -45,7 +45,8 @@ struct Params {
     int32_t mode;           // Mode
     int32_t tps;            // union teams per split-K block
     int32_t max_splits;     // gather grid.x
-    int32_t ranked;         // 1: block s takes union ranks [s*tps, (s+1)*tps); 0: team range
+    int32_t ranked;         // 1: every split slot < max_splits gets a (max, sum) pair, -inf if empty
+    int32_t balanced;       // 1 (bf16 only): block j takes the j-th of max_splits even ranges of union chunks
     double scale;           // 1 / sqrt(d)
     uint32_t *bitmaps;
     float *lnw;
@@ -60,6 +61,16 @@ struct Params {
     void *reps_out;
 };
 
+// santa_pack_pages arguments.
+struct PackParams {
+    const void *k_src;
+    const void *v_src;
+    void *k_dst;
+    void *v_dst;
+    int64_t tiles;          // num_pages * Hkv
+    int32_t dtype, T, d;
+};
+
 // Host-side argument checks; no HIP calls.
 santa_status validate_kv(const santa_kv *kv);
 
@@ -69,5 +80,6 @@ santa_status launch_select(const Params &p, void *stream);
 santa_status launch_given(const Params &p, void *stream);
 santa_status launch_gather(const Params &p, void *stream);
 santa_status launch_combine(const Params &p, void *stream);
+santa_status launch_pack_pages(const PackParams &pp, void *stream);
 
 }  // namespace santa

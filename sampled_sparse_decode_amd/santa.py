@@ -26,6 +26,7 @@ EXPORTED = (
     "santa_attend_selected",
     "dense_decode_attention",
     "santa_attention_given_teams",
+    "santa_pack_pages",
     "santa_status_string",
     "santa_version",
 )
@@ -79,6 +80,7 @@ def load():
         "santa_attend_selected": (i32, [kvp, P, i32, P, P, P, sz, P]),
         "dense_decode_attention": (i32, [kvp, P, P, P, P, sz, P]),
         "santa_attention_given_teams": (i32, [kvp, P, i32, P, P, P, P, P, sz, P]),
+        "santa_pack_pages": (i32, [i32, ctypes.c_int64, i32, i32, i32, P, P, P, P, P]),
         "santa_status_string": (ctypes.c_char_p, [i32]),
         "santa_version": (i32, []),
     }
@@ -114,12 +116,12 @@ def _stream():
 class KVCache:
     """A paged KV cache on the device, in the layout of include/santa.h.
 
-    k_pages: [num_pages][Hkv][T][d] and v_pages: [num_pages][Hkv][d][T],
-    bfloat16 or float32; page_table [B][max_pages_per_seq] int32; seq_lens
-    [B] int32.
+    k_pages, v_pages: [num_pages][Hkv][T * d] tiles in the library's tile
+    order (write them with pack_pages), bfloat16 or float32; page_table
+    [B][max_pages_per_seq] int32; seq_lens [B] int32.
     """
 
-    def __init__(self, k_pages, v_pages, page_table, seq_lens, num_q_heads):
+    def __init__(self, k_pages, v_pages, page_table, seq_lens, num_q_heads, page_size):
         for t in (k_pages, v_pages, page_table, seq_lens):
             if not t.is_contiguous():
                 raise ValueError("KV cache tensors must be contiguous")
@@ -127,13 +129,14 @@ class KVCache:
             raise ValueError("k_pages / v_pages must both be bfloat16 or float32")
         if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
             raise ValueError("page_table and seq_lens must be int32")
-        if k_pages.dim() != 4 or tuple(v_pages.shape) != (k_pages.shape[0], k_pages.shape[1],
-                                                          k_pages.shape[3], k_pages.shape[2]):
-            raise ValueError("k_pages must be [num_pages][Hkv][T][d] and v_pages [num_pages][Hkv][d][T]")
+        if k_pages.dim() != 3 or v_pages.shape != k_pages.shape or k_pages.shape[2] % int(page_size):
+            raise ValueError("k_pages and v_pages must both be [num_pages][Hkv][T * d] tiles")
         self.k_pages, self.v_pages = k_pages, v_pages
         self.page_table, self.seq_lens = page_table, seq_lens
         self.num_q_heads = int(num_q_heads)
-        self.num_pages, self.num_kv_heads, self.page_size, self.head_dim = (int(x) for x in k_pages.shape)
+        self.num_pages, self.num_kv_heads = int(k_pages.shape[0]), int(k_pages.shape[1])
+        self.page_size = int(page_size)
+        self.head_dim = int(k_pages.shape[2]) // self.page_size
         self.batch, self.max_pages_per_seq = (int(x) for x in page_table.shape)
         self.dtype = k_pages.dtype
         self.device = k_pages.device
@@ -143,6 +146,22 @@ class KVCache:
                         self.head_dim, self.page_size, self.max_pages_per_seq, 0, self.num_pages,
                         self.k_pages.data_ptr(), self.v_pages.data_ptr(),
                         self.page_table.data_ptr(), self.seq_lens.data_ptr())
+
+
+def pack_pages(k_src, v_src, k_dst=None, v_dst=None):
+    """Pages [num_pages][Hkv][T][d] -> tiles [num_pages][Hkv][T * d] in the cache's tile order."""
+    if k_src.dim() != 4 or v_src.shape != k_src.shape or k_src.dtype not in _DTYPES or v_src.dtype != k_src.dtype:
+        raise ValueError("k_src and v_src must be [num_pages][Hkv][T][d] of one cache dtype")
+    if not (k_src.is_contiguous() and v_src.is_contiguous()):
+        raise ValueError("k_src and v_src must be contiguous")
+    n, hkv, T, d = (int(x) for x in k_src.shape)
+    if k_dst is None:
+        k_dst = torch.empty((n, hkv, T * d), dtype=k_src.dtype, device=k_src.device)
+    if v_dst is None:
+        v_dst = torch.empty((n, hkv, T * d), dtype=k_src.dtype, device=k_src.device)
+    _check("santa_pack_pages", load().santa_pack_pages(_DTYPES[k_src.dtype], n, hkv, T, d, _ptr(k_src), _ptr(v_src),
+                                                      _ptr(k_dst), _ptr(v_dst), _stream()))
+    return k_dst, v_dst
 
 
 def storage_tensor(arr, dtype, device):
@@ -155,11 +174,17 @@ def storage_tensor(arr, dtype, device):
 
 
 def kv_from_workload(w, device="cuda"):
-    """Upload a workloads.Workload; returns (KVCache, q tensor)."""
-    kv = KVCache(storage_tensor(w.k_pages, w.dtype, device), storage_tensor(w.v_pages, w.dtype, device),
+    """Upload a workloads.Workload (pages [num_pages][Hkv][T][d]) and pack its
+    pages into the cache's tile order; returns (KVCache, q tensor)."""
+    k_src = storage_tensor(w.k_pages, w.dtype, device)
+    v_src = storage_tensor(w.v_pages, w.dtype, device)
+    k_pages, v_pages = pack_pages(k_src, v_src)
+    torch.cuda.current_stream().synchronize()
+    del k_src, v_src
+    kv = KVCache(k_pages, v_pages,
                  torch.from_numpy(np.ascontiguousarray(w.page_table, dtype=np.int32)).to(device),
                  torch.from_numpy(np.ascontiguousarray(w.seq_lens, dtype=np.int32)).to(device),
-                 w.num_q_heads)
+                 w.num_q_heads, w.page_size)
     return kv, storage_tensor(w.q, w.dtype, device)
 
 

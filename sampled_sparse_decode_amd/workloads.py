@@ -3,12 +3,12 @@
 This module builds the inputs that both the HIP path and the CPU oracle are
 run on: paged key/value caches, queries, page tables and sequence lengths.
 It holds none of the attention method's arithmetic; it only draws random
-numbers (numpy's default_rng, seeded) and stores them in the library's
-layout.
+numbers (numpy's default_rng, seeded) and stores them as plain arrays (the
+binding packs pages into the library's tile order on the device).
 
-Layout (shared by every entry point of the library):
+Layout:
   k_pages           [num_pages][Hkv][T][d]  bfloat16 bit patterns (uint16) or float32
-  v_pages           [num_pages][Hkv][d][T]  same type, channel-major within a page
+  v_pages           [num_pages][Hkv][T][d]  same type, token-major
   q                 [B][Hq][d]               same storage type as the cache
   page_table        [B][max_pages_per_seq]   int32 physical page of each logical team
   seq_lens          [B]                      int32 tokens per sequence
@@ -86,7 +86,7 @@ class _PagedBuilder:
         self.P = (L + T - 1) // T
         esz = np.uint16 if dtype == "bf16" else np.float32
         self.k = np.zeros((B * self.P, hkv, T, d), dtype=esz)
-        self.v = np.zeros((B * self.P, hkv, d, T), dtype=esz)
+        self.v = np.zeros((B * self.P, hkv, T, d), dtype=esz)
 
     def put(self, which, b, g, x):
         """Store float32 rows x [L][d] of sequence b, KV head g; returns the stored values as float32."""
@@ -94,10 +94,7 @@ class _PagedBuilder:
         buf = np.zeros((P * T, d), dtype=np.float32)
         buf[:self.L] = x
         st = to_storage(buf, self.dtype)
-        if which == "k":
-            self.k[b * P:(b + 1) * P, g] = st.reshape(P, T, d)
-        else:
-            self.v[b * P:(b + 1) * P, g] = st.reshape(P, T, d).transpose(0, 2, 1)
+        (self.k if which == "k" else self.v)[b * P:(b + 1) * P, g] = st.reshape(P, T, d)
         return storage_to_f32(st[:self.L], self.dtype)
 
     def workload(self, name, q, M, seed=0, offset=0, notes=None):
@@ -261,7 +258,7 @@ def paged_ragged(data_seed=5, num_seqs=16, len_min=4096, len_max=65536, T=128, M
     page_table = np.zeros((num_seqs, P), dtype=np.int32)
     esz = np.uint16 if dtype == "bf16" else np.float32
     k_pages = np.zeros((total, hkv, T, d), dtype=esz)
-    v_pages = np.zeros((total, hkv, d, T), dtype=esz)
+    v_pages = np.zeros((total, hkv, T, d), dtype=esz)
     starts = np.concatenate([[0], np.cumsum(kb)[:-1]])
     for b in range(num_seqs):
         page_table[b, :kb[b]] = perm[starts[b]:starts[b] + kb[b]]
@@ -275,7 +272,7 @@ def paged_ragged(data_seed=5, num_seqs=16, len_min=4096, len_max=65536, T=128, M
         vals = r.standard_normal((K * T, d), dtype=np.float32)
         vals[L:] = 0.0
         k_pages[ids, g] = to_storage(keys, dtype).reshape(K, T, d)
-        v_pages[ids, g] = to_storage(vals, dtype).reshape(K, T, d).transpose(0, 2, 1)
+        v_pages[ids, g] = to_storage(vals, dtype).reshape(K, T, d)
 
     _per_chunk(data_seed, num_seqs, hkv, fill)
     q = rng.standard_normal((num_seqs, hq, d), dtype=np.float32)

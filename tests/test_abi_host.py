@@ -46,7 +46,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.santa_version() == 100
+    assert lib.santa_version() == 200
     for code in range(6):
         assert S.santa_status_string(code)
     assert S.santa_status_string(99) == "unknown status"
@@ -120,3 +120,28 @@ def test_decode_argument_checks(lib):
     assert lib.santa_attention_given_teams(ctypes.byref(k), FAKE, 0, FAKE, FAKE, FAKE, None, FAKE,
                                            big, None) == SHAPE
     assert lib.santa_build_reps(ctypes.byref(k), None, None) == NULL
+
+
+def test_pack_pages_validation(lib):
+    """santa_pack_pages rejects bad arguments on the host, before any launch."""
+    F = ctypes.c_void_p
+    a, b, c, d = (F(0x10000000 * i) for i in (1, 2, 3, 4))
+    ok = dict(dtype=S.SANTA_BF16, n=8, hkv=4, T=128, d=128)
+
+    def call(**over):
+        x = dict(ok, **over)
+        ptrs = over.get("ptrs", (a, b, c, d))
+        return lib.santa_pack_pages(x["dtype"], x["n"], x["hkv"], x["T"], x["d"], *ptrs, None)
+
+    assert call(dtype=7) == UNSUP
+    assert call(d=96) == UNSUP
+    assert call(T=48) == UNSUP
+    assert call(hkv=0) == SHAPE
+    assert call(n=-1) == SHAPE
+    assert call(n=1 << 40) == SHAPE
+    assert call(n=0, ptrs=(None, None, None, None)) == OK          # nothing to do, nothing enqueued
+    assert call(ptrs=(a, b, None, d)) == NULL
+    # 8 pages x 4 heads x 128 x 128 bf16 = 1 MiB per buffer: destinations may
+    # not overlap any buffer; the two sources may
+    assert call(ptrs=(a, b, F(a.value + 4096), d)) == SHAPE
+    assert call(ptrs=(a, b, c, F(c.value + (1 << 20) - 2))) == SHAPE
