@@ -29,8 +29,14 @@ using namespace dev;
 // log w_t = -log(pi_t) (0 under full coverage), plus the optional sorted team
 // list and 1/pi.
 constexpr int kSel = 1024;
-constexpr int kSelWaves = kSel / 64;
 constexpr int kParts = 4;                          // threads per representative row
+
+// Order-preserving map of a float to a signed integer (for LDS atomicMax).
+__device__ __forceinline__ int float_key(float f) {
+    const int i = __float_as_int(f);
+    return i >= 0 ? i : (i ^ 0x7fffffff);
+}
+__device__ __forceinline__ float key_float(int k) { return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff)); }
 
 template <typename KV, int D>
 __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
@@ -39,13 +45,12 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     constexpr int ROWS = kSel / kParts;            // rows scored per pass
     __shared__ double q_s[D];
     __shared__ double e_s[kMaxTeams];              // scores, then exp(s - m)
-    __shared__ double c_s[kMaxTeams];              // inclusive cumulative sums of e
+    __shared__ double c_s[kMaxTeams];              // cumulative sums of e within a wavefront's teams
     __shared__ float lnw_s[kMaxTeams];             // log weight of each team if drawn
     __shared__ float w_s[kMaxTeams];               // 1 / pi of each team if drawn
     __shared__ uint32_t bits_s[kMaxWords];
     __shared__ int32_t wpre_s[kMaxWords + 1];
-    __shared__ double redd[kSelWaves];
-    __shared__ float redf[kSelWaves];
+    __shared__ int maxkey_s;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x;
@@ -59,6 +64,7 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     const KV *q = static_cast<const KV *>(p.q) + size_t(bh) * D;
     if (tid < D) q_s[tid] = double(to_f32(q[tid]));
     if (tid < p.words) bits_s[tid] = 0u;
+    if (tid == 0) maxkey_s = float_key(-INFINITY);
     uint4 raw[CPP];
     {
         const KV *r = reps + (size_t(row0 < p.P ? row0 : 0) * p.Hkv + g) * D + part * CPP * VPC;
@@ -71,7 +77,9 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
 
     // 1. Representative scores s_t = q . rep_t / sqrt(d) in float64 (products
     //    of two bfloat16 or two float32 values are exact in float64); four
-    //    threads per row, two partial sums each, added in a fixed order.
+    //    threads per row, two partial sums each, added in a fixed order. The
+    //    float32-rounded maximum is gathered on the way (LDS atomic max).
+    float mloc = -INFINITY;
     for (int t = row0; t < ((K + ROWS - 1) / ROWS) * ROWS; t += ROWS) {
         if (t != row0) {
             const KV *r = reps + (size_t(t < K ? t : 0) * p.Hkv + g) * D + part * CPP * VPC;
@@ -93,22 +101,23 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
         double acc = a0 + a1;
         acc += __shfl_xor(acc, 1, 64);
         acc += __shfl_xor(acc, 2, 64);
-        if (part == 0 && t < K) e_s[t] = acc * p.scale;
+        const double sc = acc * p.scale;
+        if (t < K) {
+            if (part == 0) e_s[t] = sc;
+            mloc = fmaxf(mloc, float(sc));
+        }
     }
+    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+    if (lane == 0) atomicMax(&maxkey_s, float_key(mloc));
     __syncthreads();
 
-    // 2. Team softmax numerators e_t = exp(s_t - m) and their cumulative sums
-    //    C_t, in float64. The shift m is the float32-rounded max: any shift at
-    //    or near the max cancels in C_t / C_last and in p_t = e_t / C_last.
-    //    Thread tid owns the contiguous teams [t0, t1).
-    float mf = -INFINITY;
-    for (int t = tid; t < K; t += kSel) mf = fmaxf(mf, float(e_s[t]));
-    for (int off = 32; off > 0; off >>= 1) mf = fmaxf(mf, __shfl_xor(mf, off, 64));
-    if (lane == 0) redf[wave] = mf;
-    __syncthreads();
-    float mmax = redf[0];
-    for (int i = 1; i < kSelWaves; ++i) mmax = fmaxf(mmax, redf[i]);
-    const double m = double(mmax);
+    // 2. Team softmax numerators e_t = exp(s_t - m) in float64, with the
+    //    float32-rounded max as the shift (any shift at or near the max
+    //    cancels in C_t / C_last and in p_t = e_t / C_last). Thread tid owns
+    //    the contiguous teams [tid per, (tid + 1) per); c_s holds cumulative
+    //    sums within each wavefront's range, so C_t = B_w + c_s[t] with B_w
+    //    the sum of the previous wavefronts' last entries.
+    const double m = double(key_float(maxkey_s));
     const int per = (K + kSel - 1) / kSel;
     const int t0 = min(K, tid * per), t1 = min(K, t0 + per);
     double local = 0.0;
@@ -122,18 +131,24 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
         const double y = __shfl_up(incl, off, 64);
         if (lane >= off) incl += y;
     }
-    if (lane == 63) redd[wave] = incl;
-    __syncthreads();
-    double base = 0.0;
-    for (int i = 0; i < wave; ++i) base += redd[i];
-    double run = base + incl - local;
+    double run = incl - local;
     for (int t = t0; t < t1; ++t) {
         run += e_s[t];
         c_s[t] = run;
     }
     __syncthreads();
+
+    // Wavefront bases B_w = sum of the previous wavefronts' last cumulative
+    // entries, added in wavefront order (the same way in every thread), so
+    // C is one monotone sequence and Z = C_last.
+    constexpr int kW = kSel / 64;
+    auto wave_end = [&](int w, double bw) {
+        const int lo = min(K, w * 64 * per), hi = min(K, (w + 1) * 64 * per);
+        return hi > lo ? bw + c_s[hi - 1] : bw;
+    };
+    double Z = 0.0;
+    for (int w = 0; w < kW; ++w) Z = wave_end(w, Z);
     const bool full = K > 0 && p.M >= K;
-    const double Z = K > 0 ? c_s[K - 1] : 0.0;
 
     // 3. Wavefront 0 draws; the other wavefronts compute pi_t and log w_t for
     //    every team meanwhile (pi = 1 - (1 - p)^M = -expm1(M log1p(-p))).
@@ -149,14 +164,20 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
                     const uint4 r = philox4x32_10(make_uint4(uint32_t(j) >> 2, uint32_t(h), uint32_t(b), p.offset),
                                                   p.seed_lo, p.seed_hi);
                     const uint32_t x = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
-                    const double u = (double(x) + 0.5) * 0x1p-32;
-                    const double target = u * Z;
+                    const double target = ((double(x) + 0.5) * 0x1p-32) * Z;
                     int t;
-                    if (target < c_s[K - 1]) {
-                        int lo = 0, hi = K - 1;
+                    if (target < Z) {
+                        int w = 0;                      // first wavefront whose end exceeds the target
+                        double bw = 0.0;
+                        for (;; ++w) {
+                            const double next = wave_end(w, bw);
+                            if (target < next) break;
+                            bw = next;
+                        }
+                        int lo = min(K, w * 64 * per), hi = min(K, (w + 1) * 64 * per) - 1;
                         while (lo < hi) {
                             const int mid = (lo + hi) >> 1;
-                            if (target < c_s[mid]) hi = mid; else lo = mid + 1;
+                            if (target < bw + c_s[mid]) hi = mid; else lo = mid + 1;
                         }
                         t = lo;
                     } else {        // unreachable for u < 1: last team with mass
@@ -184,18 +205,18 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
 
     // 4. Outputs: bitmap, log weights of drawn teams, optional sorted list.
     if (tid < p.words) p.bitmaps[size_t(bh) * p.words + tid] = bits_s[tid];
-    if (tid == 0) {
-        int acc = 0;
-        for (int i = 0; i < p.words; ++i) {
-            wpre_s[i] = acc;
-            acc += __popc(bits_s[i]);
-        }
-        wpre_s[p.words] = acc;
-    }
     float *lnw = p.lnw + size_t(bh) * p.P;
     for (int t = tid; t < K; t += kSel)
         if ((bits_s[t >> 5] >> (t & 31)) & 1u) lnw[t] = lnw_s[t];
     if (p.sampled) {
+        if (tid == 0) {
+            int acc = 0;
+            for (int i = 0; i < p.words; ++i) {
+                wpre_s[i] = acc;
+                acc += __popc(bits_s[i]);
+            }
+            wpre_s[p.words] = acc;
+        }
         __syncthreads();
         for (int t = tid; t < K; t += kSel) {
             const uint32_t word = bits_s[t >> 5];
