@@ -570,7 +570,9 @@ __device__ void chunk_window(const Params &p, GroupChunks &gc, int cpt, int c0, 
     __syncthreads();
 }
 
-template <int D>
+// MODE (kModeSanta or kModeDense, equal to p.mode) is a template argument
+// so the two uses show up as separate kernels in a profile.
+template <int D, int MODE>
 __global__ __launch_bounds__(kBlock, 3) void gather_balanced_kernel(Params p) {
     constexpr int NT = D / 16;
     struct Stream {
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(kBlock, 3) void gather_balanced_kernel(Params p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, g4 = lane >> 4;
     const int hbase = b * p.Hq + g * p.G;
-    const bool dense = p.mode == kModeDense;
+    constexpr bool dense = MODE == kModeDense;
 
     fill_q_lds<D>(p, lds.st.q_lds, hbase);
     const int U = group_union(p, gc, g, b);
@@ -882,8 +884,13 @@ santa_status launch_gather(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(p.max_splits, p.Hkv, p.B);
     if (p.dtype == SANTA_BF16 && p.balanced) {
-        if (p.d == 64) hipLaunchKernelGGL((gather_balanced_kernel<64>), grid, dim3(kBlock), 0, st, p);
-        else hipLaunchKernelGGL((gather_balanced_kernel<128>), grid, dim3(kBlock), 0, st, p);
+        if (p.mode == kModeDense) {
+            if (p.d == 64) hipLaunchKernelGGL((gather_balanced_kernel<64, kModeDense>), grid, dim3(kBlock), 0, st, p);
+            else hipLaunchKernelGGL((gather_balanced_kernel<128, kModeDense>), grid, dim3(kBlock), 0, st, p);
+        } else {
+            if (p.d == 64) hipLaunchKernelGGL((gather_balanced_kernel<64, kModeSanta>), grid, dim3(kBlock), 0, st, p);
+            else hipLaunchKernelGGL((gather_balanced_kernel<128, kModeSanta>), grid, dim3(kBlock), 0, st, p);
+        }
     } else if (p.dtype == SANTA_BF16) {
         if (p.d == 64) hipLaunchKernelGGL((gather_mfma_kernel<64>), grid, dim3(kBlock), 0, st, p);
         else hipLaunchKernelGGL((gather_mfma_kernel<128>), grid, dim3(kBlock), 0, st, p);

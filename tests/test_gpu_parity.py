@@ -48,6 +48,9 @@ SMALL = {
                                                            M=40, hq=8, hkv=2, d=64),
     "f32_b16_t16_union_rank": lambda: W.qwen_planted(batch=16, seq_len=4500, T=16, M=50, hq=8, hkv=2, d=64,
                                                      plants=4, dtype="f32"),
+    # a full 16-head group over 300 small teams
+    "bf16_g16_p300": lambda: W.qwen_planted(batch=1, seq_len=4800, T=16, M=40, hq=16, hkv=1, d=64,
+                                                        plants=3),
 }
 
 
@@ -130,6 +133,29 @@ def test_santa_parity(name):
             _, f = parity.check_santa_head(w, okv, reps, b, h, out[b, h], lse[b, h], teams[b, h], inv_pi[b, h])
             flips += f
     say(f"  near-tie flips: {flips}")
+
+
+@pytest.mark.parametrize("name", ["qwen_bf16_ragged", "mixture_t256", "bf16_g16_p300",
+                                  "f32_d128_t64_g2"])
+def test_decode_equals_select_then_attend(name):
+    """santa_decode_attention and santa_select_teams + santa_attend_selected on
+    one workspace give bit-identical results (sets, weights, outputs)."""
+    w = SMALL[name]()
+    say(f"[decode == select + attend] {name}")
+    kv, q = S.kv_from_workload(w)
+    reps = S.santa_build_reps(kv)
+    a = run_santa(w, kv, q, reps)
+    ws = S.make_workspace(kv, w.M)
+    B, Hq = w.batch, w.num_q_heads
+    teams = torch.empty((B, Hq, w.M), dtype=torch.int32, device="cuda")
+    inv_pi = torch.empty((B, Hq, w.M), dtype=torch.float32, device="cuda")
+    S.santa_select_teams(kv, q, reps, w.M, w.seed, w.offset, ws, teams, inv_pi)
+    out = torch.empty((B, Hq, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    S.santa_attend_selected(kv, q, w.M, ws, out, lse)
+    torch.cuda.synchronize()
+    for x, y in zip(a, (out.cpu().numpy(), lse.cpu().numpy(), teams.cpu().numpy(), inv_pi.cpu().numpy())):
+        assert np.array_equal(x, y)
 
 
 def test_santa_deterministic_and_seeded():
