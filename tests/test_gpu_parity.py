@@ -48,6 +48,9 @@ SMALL = {
                                                            M=40, hq=8, hkv=2, d=64),
     "f32_b16_t16_union_rank": lambda: W.qwen_planted(batch=16, seq_len=4500, T=16, M=50, hq=8, hkv=2, d=64,
                                                      plants=4, dtype="f32"),
+    # the longest page table (2048 teams of 16 tokens), 16-head groups
+    "bf16_b3_g16_p2048": lambda: W.qwen_planted(batch=3, seq_len=32768, T=16, M=24, hq=48, hkv=3,
+                                                            d=64, plants=2),
     # a full 16-head group over 300 small teams
     "bf16_g16_p300": lambda: W.qwen_planted(batch=1, seq_len=4800, T=16, M=40, hq=16, hkv=1, d=64,
                                                         plants=3),
