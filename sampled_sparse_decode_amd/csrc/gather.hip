@@ -10,19 +10,23 @@
 //         section 三 steps 4-5 (exact scores inside sampled teams, importance
 //         re-weighting).
 //
-// A gather block (split s, KV head g, sequence b) owns teams
-// [s * tps, (s + 1) * tps) of sequence b (tps divides 32, so their bits sit in
-// one bitmap word). It reads the group's bitmap word, the teams' log weights
-// and page ids in one round trip, keeps the teams some query head of g drew
-// (dense mode: every team, every head, weight 0 in log space), streams each
-// kept team's K and V tile from HBM exactly once, scores it for the heads that
-// drew it, and runs an online softmax in which the team weight w is folded
-// into the logit (s_j + log w): numerator and denominator both carry w, and
-// nothing overflows however large 1/pi gets. It writes one partial (max, sum,
-// weighted value sum) per head that drew a team of the split, at slot s. The
-// combine kernel reads the head's bitmap to know which slots hold partials and
-// merges them in split order. Blocks whose teams nobody drew exit after the
-// first round trip.
+// Every gather block works for one (sequence b, KV head g) group: it streams
+// the K and V chunks of teams some query head of g drew (dense mode: every
+// team, every head, weight 0 in log space) from HBM exactly once, scores them
+// for the heads that drew them, and runs an online softmax in which the team
+// weight w is folded into the logit (s_j + log w): numerator and denominator
+// both carry w, and nothing overflows however large 1/pi gets. It writes one
+// partial (max, sum, weighted value sum) per head of g at its split slot; the
+// combine merges a head's partials in slot order.
+//
+// Two block shapes:
+//   bf16 caches  balanced blocks (gather_balanced_kernel, matrix cores): the
+//                group's drawn chunks, listed by union rank, cut into even
+//                contiguous ranges, one per block.
+//   fp32 caches  team-range blocks (gather_f32_kernel, float64 scores): block
+//                s owns teams [s tps, (s + 1) tps) (tps divides 32, so their
+//                bits sit in one bitmap word), or with union ranks the drawn
+//                teams of ranks [s tps, (s + 1) tps).
 //
 // Cache layout: each (page, KV head) tile is cut into chunks of 32 tokens;
 // keys are stored as 32-channel slabs [32 tokens][32 channels] and values
@@ -38,7 +42,8 @@ using namespace dev;
 
 constexpr int kGM = kMaxGroup;     // head slots per KV head (16)
 
-// Per-block team list, filled by load_team_list.
+// Per-block team list of the fp32 gather, filled by load_team_list or
+// load_ranked_team_list.
 struct TeamList {
     int64_t page[kMaxTeamsPerSplit];
     int32_t n[kMaxTeamsPerSplit];          // valid tokens of the team
@@ -245,13 +250,6 @@ __device__ __forceinline__ void mfma_load_chunk_at(const Params &p, int64_t page
     for (int nt = 0; nt < MfmaChunk<D>::NT; ++nt) c.v[nt] = ld16(col + (16 * nt) * C);
 }
 
-template <int D>
-__device__ __forceinline__ void mfma_load_chunk(const Params &p, const TeamList &tl, int q, int cpt, int g,
-                                                int i16, int g4, MfmaChunk<D> &c) {
-    const int ti = q / cpt;
-    mfma_load_chunk_at<D>(p, tl.page[ti], tl.n[ti], (q - ti * cpt) * 32, g, i16, g4, c);
-}
-
 // Zero the bf16 elements e >= keep of a 16-byte operand (ragged team tails).
 __device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
     if (keep >= 8) return v;
@@ -341,15 +339,6 @@ __device__ __forceinline__ void mfma_compute_chunk_at(const Params &p, int n, in
     }
 }
 
-template <int D>
-__device__ __forceinline__ void mfma_compute_chunk(const Params &p, const TeamList &tl, int q, int cpt,
-                                                   int i16, int g4, const bf16_t (*q_lds)[D + 8],
-                                                   const MfmaChunk<D> &c, float &m, float &lsum,
-                                                   f32x4 (&o)[D / 16]) {
-    const int ti = q / cpt;
-    mfma_compute_chunk_at<D>(p, tl.n[ti], (q - ti * cpt) * 32, tl.lnw[ti][i16], i16, g4, q_lds, c, m, lsum, o);
-}
-
 // Cross-wavefront merge of the online-softmax states and the store of the
 // block's partial at slot s of every head of the group.
 template <int D>
@@ -425,51 +414,6 @@ __device__ __forceinline__ void fill_q_lds(const Params &p, bf16_t (*q_lds)[D + 
                                   : make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4 *>(&q_lds[h][cc * 8]) = v;
     }
-}
-
-template <int D>
-__global__ __launch_bounds__(kBlock, 3) void gather_mfma_kernel(Params p) {
-    constexpr int NT = D / 16;
-    struct Stream {
-        TeamList tl;
-        __attribute__((aligned(16))) bf16_t q_lds[kGM][D + 8];
-    };
-    __shared__ union {
-        Stream st;
-        MfmaReduce<D> rd;                         // used once the chunk loop is done
-    } lds;
-    TeamList &tl = lds.st.tl;
-    bf16_t (*q_lds)[D + 8] = lds.st.q_lds;
-
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int i16 = lane & 15, g4 = lane >> 4;
-    const int G = p.G;
-    const int hbase = b * p.Hq + g * G;
-
-    fill_q_lds<D>(p, q_lds, hbase);
-    const int nteams = p.ranked ? load_ranked_team_list(p, tl, s, g, b) : load_team_list(p, tl, s, g, b);
-    if (nteams == 0) {
-        if (p.ranked && tid < G) write_empty_partial(p, hbase + tid, s);
-        return;
-    }
-
-    const int cpt = p.T >= 32 ? p.T / 32 : 1;
-    const int nchunks = nteams * cpt;
-    float m = kNegInfF, lsum = 0.0f;
-    f32x4 o[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Chunk loop: a wavefront's 16 loads of a chunk (16 KiB at d = 128) are
-    // all in flight before the first use; the other resident blocks (three
-    // per CU) cover the wait.
-    for (int q = wave; q < nchunks; q += kWaves) {
-        MfmaChunk<D> ck;
-        mfma_load_chunk<D>(p, tl, q, cpt, g, i16, g4, ck);
-        mfma_compute_chunk<D>(p, tl, q, cpt, i16, g4, q_lds, ck, m, lsum, o);
-    }
-    mfma_store_partial<D>(p, lds.rd, m, lsum, o, hbase, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -746,6 +690,7 @@ __global__ __launch_bounds__(kBlock) void gather_f32_kernel(Params p) {
 // the value sums of the slots that hold partials, as float4, all at once.
 // ---------------------------------------------------------------------------
 constexpr int kCombine = 256;
+constexpr int kFew = 8;                            // value quads per thread of the one-round-trip combine
 
 template <int D>
 __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
@@ -766,6 +711,97 @@ __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
     const int b = bh / p.Hq;
     const bool dense = p.mode == kModeDense;
     const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + size_t(bh) * p.P;
+    const float4 *pacc = reinterpret_cast<const float4 *>(p.part_acc + size_t(bh) * p.P * D);
+    const int c4 = tid % Q4, sb = tid / Q4;
+
+    if (p.max_splits <= kFew * SUB) {
+        // Few slots (every balanced split at batch >= 1 up to 64 / 128 slots):
+        // one round trip. Every slot's (max, sum) and this thread's quads of
+        // every slot's value sum are loaded at once; slots that hold no
+        // partial of this call get weight 0 and their values are never used.
+        __shared__ float2 ml_s[kFew * SUB];
+        const int Lraw = p.seq_lens[b];
+        if (!dense && !p.ranked && tid < p.words) hw_s[tid] = p.bitmaps[size_t(bh) * p.words + tid];
+        if (tid < p.max_splits) ml_s[tid] = ml[tid];
+        float4 x[kFew];
+#pragma unroll
+        for (int u = 0; u < kFew; ++u) {
+            const int sp = sb + u * SUB;
+            x[u] = (sp < p.max_splits) ? pacc[size_t(sp) * Q4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int L = clamp_len(Lraw, p.P * p.T);
+            const int K = (L + p.T - 1) / p.T;
+            const int nslots = (K + p.tps - 1) / p.tps;
+            const uint32_t low = (p.tps >= 32) ? 0xffffffffu : ((1u << p.tps) - 1u);
+            float mv[2];
+            bool ok[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int sp = lane + 64 * i;
+                bool hv = sp < p.max_splits;
+                if (hv) {
+                    if (p.ranked) {
+                        hv = ml_s[sp].x != kNegInfF;
+                    } else {
+                        hv = sp < nslots;
+                        if (hv && !dense) {
+                            const int t0 = sp * p.tps;
+                            hv = ((hw_s[t0 >> 5] >> (t0 & 31)) & low) != 0u;
+                        }
+                    }
+                }
+                ok[i] = hv;
+                mv[i] = hv ? ml_s[sp].x : kNegInfF;
+            }
+            float mstar = fmaxf(mv[0], mv[1]);
+            for (int off = 32; off > 0; off >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, off, 64));
+            float lpart = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int sp = lane + 64 * i;
+                const float f = ok[i] ? expf(mv[i] - mstar) : 0.0f;
+                if (sp < kFew * SUB) f_s[sp] = f;
+                if (ok[i]) lpart += f * ml_s[sp].y;
+            }
+            for (int off = 32; off > 0; off >>= 1) lpart += __shfl_xor(lpart, off, 64);
+            if (lane == 0) {
+                redf[0] = mstar;
+                redf[1] = lpart;
+            }
+        }
+        __syncthreads();
+        const float mstar = redf[0], l = redf[1];
+        if (mstar == kNegInfF) {                  // no partial: empty sequence
+            for (int c = tid; c < D; c += kCombine) p.out[size_t(bh) * D + c] = 0.0f;
+            if (tid == 0 && p.lse) p.lse[bh] = kNegInfF;
+            return;
+        }
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < kFew; ++u) {
+            const int sp = sb + u * SUB;
+            const float f = (sp < p.max_splits) ? f_s[sp] : 0.0f;
+            if (f > 0.0f) {
+                a.x += f * x[u].x; a.y += f * x[u].y; a.z += f * x[u].z; a.w += f * x[u].w;
+            }
+        }
+        acc_s[sb][c4] = a;
+        __syncthreads();
+        if (tid < Q4) {
+            float4 sum = acc_s[0][tid];
+            for (int i = 1; i < SUB; ++i) {
+                const float4 y = acc_s[i][tid];
+                sum.x += y.x; sum.y += y.y; sum.z += y.z; sum.w += y.w;
+            }
+            const float inv = 1.0f / l;
+            reinterpret_cast<float4 *>(p.out + size_t(bh) * D)[tid] =
+                make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+            if (tid == 0 && p.lse) p.lse[bh] = mstar + logf(l);
+        }
+        return;
+    }
 
     // Round trip 1. Slot (max, sum) values are read for every slot that can
     // exist (all inside the workspace); stale ones are ignored below.
@@ -844,15 +880,13 @@ __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
 
     // Round trip 2: value sums, thread (quad c4, subset sb) takes list
     // entries sb, sb + SUB, ... in batches whose loads are all issued first.
-    const int c4 = tid % Q4, sb = tid / Q4;
-    const float4 *pacc = reinterpret_cast<const float4 *>(p.part_acc + size_t(bh) * p.P * D) + c4;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k0 = sb; k0 < total; k0 += BATCH * SUB) {
         float4 x[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
             const int k = k0 + u * SUB;
-            x[u] = (k < total) ? pacc[size_t(list_s[k]) * Q4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            x[u] = (k < total) ? pacc[size_t(list_s[k]) * Q4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
@@ -892,8 +926,7 @@ santa_status launch_gather(const Params &p, void *stream) {
             else hipLaunchKernelGGL((gather_balanced_kernel<128, kModeSanta>), grid, dim3(kBlock), 0, st, p);
         }
     } else if (p.dtype == SANTA_BF16) {
-        if (p.d == 64) hipLaunchKernelGGL((gather_mfma_kernel<64>), grid, dim3(kBlock), 0, st, p);
-        else hipLaunchKernelGGL((gather_mfma_kernel<128>), grid, dim3(kBlock), 0, st, p);
+        return SANTA_ERR_UNSUPPORTED;             // bf16 caches always take balanced blocks
     } else {
         if (p.d == 64) hipLaunchKernelGGL((gather_f32_kernel<64>), grid, dim3(kBlock), 0, st, p);
         else hipLaunchKernelGGL((gather_f32_kernel<128>), grid, dim3(kBlock), 0, st, p);
