@@ -1,6 +1,6 @@
 """Benchmark of SANTA++ decode attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers R]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers R] [--scale NAMES]
 
 A step is one SANTA++ decode-attention call (representative scoring, team
 softmax, draws, inclusion probabilities, split-K gather, combine) for one
@@ -13,8 +13,10 @@ before timing starts. Each call is timed as GPU time per call from HIP-graph
 replays (one call per layer captured, graph replayed), with the eager-launch
 figure reported alongside. The same is timed for the dense decode kernel, and
 for the gather + combine stage alone (the kernels that move the bytes), whose
-algorithmic bytes give the roofline figure. The CPU oracle is timed on a
-bounded sample of the same workload at the end.
+algorithmic bytes give the roofline figure. Two larger configurations (batch
+8 at 32K, batch 4 at 128K) are then measured the same way with fewer steps
+and reported compactly under "at_scale". The CPU oracle is timed on a
+bounded sample of the headline workload at the end.
 
 Prints one JSON line.
 """
@@ -46,6 +48,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate", action="store_true", help="also run plain 64 MiB device copies (counter scale)")
+    ap.add_argument("--scale", default="qwen7b_32k_b8_m32,mixture_128k_b4_t256_m64",
+                    help="workloads also measured, compactly, after the headline one ('' = none)")
+    ap.add_argument("--scale-steps", type=int, default=100)
     return ap.parse_args()
 
 
@@ -174,6 +179,67 @@ def cpu_baseline(w, budget_s):
                       f"representatives precomputed; scaled to one layer"}
 
 
+def measure(w, steps, warmup, layers, torch, S, calibrate=False):
+    """Times SANTA++, dense and the attend stage on workload w (inputs resident,
+    the layer's cache cycled over R copies). Returns a dict of results."""
+    dev = torch.device("cuda:0")
+    kv0, q = S.kv_from_workload(w, dev)
+    kv_bytes = 2 * kv0.k_pages.numel() * kv0.k_pages.element_size()
+    R = layers or max(4, math.ceil(4 * LLC_BYTES / kv_bytes))
+    cache = [kv0]
+    for _ in range(R - 1):
+        cache.append(S.KVCache(kv0.k_pages.clone(), kv0.v_pages.clone(), kv0.page_table, kv0.seq_lens,
+                               w.num_q_heads, w.page_size))
+    reps = [S.santa_build_reps(kv) for kv in cache]
+    M = w.M
+    wss = [S.make_workspace(kv, M) for kv in cache]
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    # Sets of this step (identical on every layer copy) for the byte count.
+    _, _, sampled, _ = S.santa_decode_attention(kv0, q, reps[0], M, w.seed, w.offset, wss[0], return_sets=True)
+    torch.cuda.synchronize()
+    ab = algorithmic_bytes(w, union_stats(w, sampled.cpu().numpy()))
+
+    def santa_step(i):
+        j = i % R
+        S.santa_decode_attention(cache[j], q, reps[j], M, w.seed, w.offset, wss[j], out, lse)
+
+    def dense_step(i):
+        j = i % R
+        S.dense_decode_attention(cache[j], q, wss[j], out, lse)
+
+    def attend_step(i):
+        j = i % R
+        S.santa_attend_selected(cache[j], q, M, wss[j], out, lse)
+
+    # Eager (stream) timings, then HIP-graph replay timings of the same calls.
+    r = dict(R=R, ab=ab)
+    r["santa_stream_us"] = time_stream(santa_step, steps, warmup, torch)
+    r["dense_stream_us"] = time_stream(dense_step, steps, warmup, torch)
+    r["santa_us"], r["timed_steps"] = time_graph(santa_step, R, steps, warmup, torch)
+    r["dense_us"], _ = time_graph(dense_step, R, steps, warmup, torch)
+    for j in range(R):
+        S.santa_select_teams(cache[j], q, reps[j], M, w.seed, w.offset, wss[j])
+    torch.cuda.synchronize()
+    r["attend_us"], _ = time_graph(attend_step, R, steps, warmup, torch)
+    if calibrate:
+        # Plain device copies of a known size, so rocprofv3 FETCH_SIZE / WRITE_SIZE
+        # counters can be scaled (bytes per counter unit).
+        src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    del cache, reps, wss
+    return r
+
+
+def gbps(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -183,68 +249,20 @@ def main():
     import torch
     from sampled_sparse_decode_amd import santa as S, workloads as W
 
+    torch.cuda.set_device(torch.device("cuda:0"))
     w = W.FULL_SIZE[args.workload]()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    kv0, q = S.kv_from_workload(w, dev)
-    kv_bytes = 2 * kv0.k_pages.numel() * kv0.k_pages.element_size()
-    R = args.layers or max(4, math.ceil(4 * LLC_BYTES / kv_bytes))
-    layers = [kv0]
-    for _ in range(R - 1):
-        layers.append(S.KVCache(kv0.k_pages.clone(), kv0.v_pages.clone(), kv0.page_table, kv0.seq_lens,
-                                w.num_q_heads, w.page_size))
-    reps = [S.santa_build_reps(kv) for kv in layers]
-    M = w.M
-    wss = [S.make_workspace(kv, M) for kv in layers]
-    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
-    # Sets of this step (identical on every layer copy) for the byte count.
-    _, _, sampled, _ = S.santa_decode_attention(kv0, q, reps[0], M, w.seed, w.offset, wss[0], return_sets=True)
-    torch.cuda.synchronize()
-    stats = union_stats(w, sampled.cpu().numpy())
-    ab = algorithmic_bytes(w, stats)
-
-    def santa_step(i):
-        j = i % R
-        S.santa_decode_attention(layers[j], q, reps[j], M, w.seed, w.offset, wss[j], out, lse)
-
-    def dense_step(i):
-        j = i % R
-        S.dense_decode_attention(layers[j], q, wss[j], out, lse)
-
-    def attend_step(i):
-        j = i % R
-        S.santa_attend_selected(layers[j], q, M, wss[j], out, lse)
-
-    # Eager (stream) timings, then HIP-graph replay timings of the same calls.
-    santa_stream_us = time_stream(santa_step, args.steps, args.warmup, torch)
-    dense_stream_us = time_stream(dense_step, args.steps, args.warmup, torch)
-    santa_us, timed_steps = time_graph(santa_step, R, args.steps, args.warmup, torch)
-    dense_us, _ = time_graph(dense_step, R, args.steps, args.warmup, torch)
-    for j in range(R):
-        S.santa_select_teams(layers[j], q, reps[j], M, w.seed, w.offset, wss[j])
-    torch.cuda.synchronize()
-    attend_us, _ = time_graph(attend_step, R, args.steps, args.warmup, torch)
-    if args.calibrate:
-        # Plain device copies of a known size, so rocprofv3 FETCH_SIZE / WRITE_SIZE
-        # counters can be scaled (bytes per counter unit).
-        src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-
-    attend_gbps = ab["attend"] / (attend_us * 1e-6) / 1e9
-    step_gbps = ab["step"] / (santa_us * 1e-6) / 1e9
-    dense_gbps = ab["dense"] / (dense_us * 1e-6) / 1e9
+    r = measure(w, args.steps, args.warmup, args.layers, torch, S, args.calibrate)
+    ab = r["ab"]
+    santa_us, dense_us, attend_us = r["santa_us"], r["dense_us"], r["attend_us"]
+    attend_gbps = gbps(ab["attend"], attend_us)
+    step_gbps = gbps(ab["step"], santa_us)
+    dense_gbps = gbps(ab["dense"], dense_us)
     result = {
         "metric": METRIC,
         "value": round(santa_us, 3),
         "unit": "us/layer",
         "n_gpus": 1,
-        "steps": timed_steps,
+        "steps": r["timed_steps"],
         "warmup": args.warmup,
         "ms_per_step": round(santa_us / 1e3, 6),
         "higher_is_better": False,
@@ -254,12 +272,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": int(w.seq_lens.max()),
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "team_size": w.page_size, "M": M, "layers_cycled": R},
+                   "team_size": w.page_size, "M": w.M, "layers_cycled": r["R"]},
         "timing": "HIP-graph replay of one call per layer; eager stream figures alongside",
-        "santa": {"us_per_layer": round(santa_us, 3), "us_per_layer_stream": round(santa_stream_us, 3),
+        "santa": {"us_per_layer": round(santa_us, 3), "us_per_layer_stream": round(r["santa_stream_us"], 3),
                   "hbm_gbps": round(step_gbps, 1), "pct_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
                   "bytes": ab["step"]},
-        "dense": {"us_per_layer": round(dense_us, 3), "us_per_layer_stream": round(dense_stream_us, 3),
+        "dense": {"us_per_layer": round(dense_us, 3), "us_per_layer_stream": round(r["dense_stream_us"], 3),
                   "hbm_gbps": round(dense_gbps, 1), "pct_peak": round(100 * dense_gbps / HBM_PEAK_GBPS, 2),
                   "bytes": ab["dense"]},
         "speedup_vs_dense": round(dense_us / santa_us, 3),
@@ -270,6 +288,22 @@ def main():
                      "traffic": recorded_traffic(args.workload),
                      "us_per_launch": round(attend_us, 3), "bytes_per_launch": ab["attend"]},
     }
+    # The other configurations, compactly: same timing method, fewer steps.
+    scale = {}
+    for name in [x for x in args.scale.split(",") if x and x != args.workload]:
+        ws = W.FULL_SIZE[name]()
+        rs = measure(ws, args.scale_steps, max(10, args.scale_steps // 10), 0, torch, S)
+        a = rs["ab"]
+        scale[name] = {"santa_us": round(rs["santa_us"], 2), "dense_us": round(rs["dense_us"], 2),
+                       "speedup_vs_dense": round(rs["dense_us"] / rs["santa_us"], 3),
+                       "attend_us": round(rs["attend_us"], 2),
+                       "attend_frac_of_peak": round(gbps(a["attend"], rs["attend_us"]) / HBM_PEAK_GBPS, 4),
+                       "dense_frac_of_peak": round(gbps(a["dense"], rs["dense_us"]) / HBM_PEAK_GBPS, 4),
+                       "kv_read_fraction_hbm": round(a["frac_hbm"], 4)}
+        del ws
+        torch.cuda.empty_cache()
+    if scale:
+        result["at_scale"] = scale
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
