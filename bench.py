@@ -10,8 +10,8 @@ about 1 GiB in total) and the steps cycle through them, so every step reads
 HBM rather than the 256 MB last-level cache, as a real decode step does when
 it moves from one layer's cache to the next. Inputs are resident in HBM
 before timing starts. Each call is timed as GPU time per call from HIP-graph
-replays (one call per layer captured, graph replayed), with the eager-launch
-figure reported alongside. The same is timed for the dense decode kernel, and
+replays (one call per layer captured, graph replayed; the median of three
+timed loops), with the eager-launch figure reported alongside. The same is timed for the dense decode kernel, and
 for the gather + combine stage alone (the kernels that move the bytes), whose
 algorithmic bytes give the roofline figure. Two larger configurations (batch
 8 at 32K, batch 4 at 128K) are then measured the same way with fewer steps
@@ -115,6 +115,12 @@ def time_stream(fn, steps, warmup, torch):
     return start.elapsed_time(end) * 1e3 / steps       # microseconds per call
 
 
+def median_graph(fn, R, steps, warmup, torch, loops=3):
+    """Median over `loops` timed replay loops of time_graph; returns (us, calls per loop)."""
+    runs = [time_graph(fn, R, steps, warmup, torch) for _ in range(loops)]
+    return sorted(t for t, _ in runs)[loops // 2], runs[0][1]
+
+
 def time_graph(fn, R, steps, warmup, torch):
     """GPU time per call: one call per layer captured in a HIP graph, replayed;
     HIP events around the replays on the stream they run on."""
@@ -158,24 +164,45 @@ def recorded_traffic(workload_name):
     return int(rec["read_bytes"] + rec["write_bytes"])
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the same step."""
+    """The CPU oracle, as it stands, on a bounded sample of the same step,
+    held to one thread (BLAS pools limited to 1): SANTA++ heads, then dense
+    heads, each for about half the budget."""
+    from threadpoolctl import threadpool_limits
     from oracle import numerics, santa as osanta
     kv = osanta.PagedKV(w.dtype, w.k_pages, w.v_pages, w.page_table, w.seq_lens)
     heads = [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
     reps = osanta.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
     qs = {bh: numerics.decode(w.q[bh], w.dtype) for bh in heads}
-    done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and done < len(heads) * 4:
-        b, h = heads[done % len(heads)]
-        osanta.santa_head(kv, qs[(b, h)], reps, b, h, w.num_q_heads, w.M, w.seed, done // len(heads))
-        done += 1
-    el = time.perf_counter() - t0
-    us_per_layer = el / done * len(heads) * 1e6
-    return {"value": round(us_per_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (sequence, query head) SANTA++ evaluations of {w.name} "
-                      f"({len(heads)} per layer), single-threaded float64 Python/numpy oracle, "
+
+    def timed(fn):
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s / 2 and done < len(heads) * 4:
+            fn(done)
+            done += 1
+        return (time.perf_counter() - t0) / done * len(heads) * 1e6, done
+
+    with threadpool_limits(limits=1):
+        santa_us, n_santa = timed(lambda i: osanta.santa_head(
+            kv, qs[heads[i % len(heads)]], reps, heads[i % len(heads)][0], heads[i % len(heads)][1],
+            w.num_q_heads, w.M, w.seed, i // len(heads)))
+        dense_us, n_dense = timed(lambda i: osanta.dense_head(
+            kv, qs[heads[i % len(heads)]], heads[i % len(heads)][0], heads[i % len(heads)][1], w.num_q_heads))
+    return {"value": round(santa_us, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "dense_value": round(dense_us, 1), "cpu": cpu_model(),
+            "sample": f"{n_santa} SANTA++ and {n_dense} dense (sequence, query head) evaluations of {w.name} "
+                      f"({len(heads)} per layer), float64 Python/numpy oracle on one thread, "
                       f"representatives precomputed; scaled to one layer"}
 
 
@@ -218,12 +245,12 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False):
     r = dict(R=R, ab=ab)
     r["santa_stream_us"] = time_stream(santa_step, steps, warmup, torch)
     r["dense_stream_us"] = time_stream(dense_step, steps, warmup, torch)
-    r["santa_us"], r["timed_steps"] = time_graph(santa_step, R, steps, warmup, torch)
-    r["dense_us"], _ = time_graph(dense_step, R, steps, warmup, torch)
+    r["santa_us"], r["timed_steps"] = median_graph(santa_step, R, steps, warmup, torch)
+    r["dense_us"], _ = median_graph(dense_step, R, steps, warmup, torch)
     for j in range(R):
         S.santa_select_teams(cache[j], q, reps[j], M, w.seed, w.offset, wss[j])
     torch.cuda.synchronize()
-    r["attend_us"], _ = time_graph(attend_step, R, steps, warmup, torch)
+    r["attend_us"], _ = median_graph(attend_step, R, steps, warmup, torch)
     if calibrate:
         # Plain device copies of a known size, so rocprofv3 FETCH_SIZE / WRITE_SIZE
         # counters can be scaled (bytes per counter unit).
@@ -273,7 +300,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": int(w.seq_lens.max()),
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "team_size": w.page_size, "M": w.M, "layers_cycled": r["R"]},
-        "timing": "HIP-graph replay of one call per layer; eager stream figures alongside",
+        "timing": "HIP-graph replay of one call per layer, median of 3 timed loops of `steps` calls; "
+                  "eager stream figures alongside",
         "santa": {"us_per_layer": round(santa_us, 3), "us_per_layer_stream": round(r["santa_stream_us"], 3),
                   "hbm_gbps": round(step_gbps, 1), "pct_peak": round(100 * step_gbps / HBM_PEAK_GBPS, 2),
                   "bytes": ab["step"]},
