@@ -128,6 +128,22 @@ santa_status santa_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes);
  * Run once after prefill, and for a team again after its keys change. */
 santa_status santa_build_reps(const santa_kv *kv, void *reps, void *stream);
 
+/* Representative upkeep after an append ([EXP] section 三 step 2: one
+ * representative per team, here kept equal to the team mean as tokens
+ * arrive). For each sequence b, recomputes reps[b][t] for the teams that
+ * received tokens since the lengths were prev_seq_lens[b], i.e. teams
+ * floor(prev_seq_lens[b] / T) .. K_b - 1 (at most ceil(max_new_tokens / T) + 1
+ * of them), with the arithmetic of santa_build_reps, so the result equals a
+ * full rebuild bit for bit. The new keys must already be in the pages and
+ * kv->seq_lens must hold the new lengths.
+ *   reps           as for santa_build_reps; rows of other teams untouched
+ *   prev_seq_lens  [B] int32, device: lengths before the append, each <= the
+ *                  new length (a smaller new length refreshes nothing)
+ *   max_new_tokens host bound on the tokens appended to any one sequence
+ *                  (>= 0; 0 enqueues nothing) */
+santa_status santa_update_reps(const santa_kv *kv, void *reps, const int32_t *prev_seq_lens,
+                               int32_t max_new_tokens, void *stream);
+
 /* SANTA++ decode attention ([ABS]; [EXP] section 三 steps 2-7).
  * For each sequence b and query head h (KV head g):
  *   1. s_t = q . reps[b][t][g] / sqrt(d), summed in float64;

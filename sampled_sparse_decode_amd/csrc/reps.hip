@@ -8,7 +8,9 @@
 //
 // rep = round_to_cache_type(sum of the team's n valid keys / n): float64 sums
 // (exact for bfloat16 keys), one correctly rounded float64 divide, one
-// rounding to nearest even into the cache type.
+// rounding to nearest even into the cache type. The same kernel refreshes
+// only the teams that received appended tokens (update mode), with the same
+// arithmetic, so an updated row equals a rebuilt one bit for bit.
 #include "device_common.h"
 
 namespace santa {
@@ -27,9 +29,13 @@ __global__ __launch_bounds__(kBlock) void build_reps_kernel(Params p) {
     constexpr int UNROLL = 8;
     __shared__ double part_s[RL][D];
 
-    const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int L = clamp_len(p.seq_lens[b], p.P * p.T);
     const int K = (L + p.T - 1) / p.T;
+    // Update mode: block x recomputes team first + x, first being the team
+    // that held the sequence's token prev_len (the first appended token).
+    const int first = p.prev_lens ? clamp_len(p.prev_lens[b], p.P * p.T) / p.T : 0;
+    const int t = first + blockIdx.x;
     if (t >= K) return;
     const int64_t page = clamp_page(p.page_table[size_t(b) * p.P + t], p.num_pages);
     const int n = min(p.T, L - t * p.T);
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kBlock) void build_reps_kernel(Params p) {
 
 santa_status launch_build_reps(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(p.P, p.Hkv, p.B);
+    const dim3 grid(p.prev_lens ? p.update_teams : p.P, p.Hkv, p.B);
     if (p.dtype == SANTA_BF16) {
         if (p.d == 64) hipLaunchKernelGGL((build_reps_kernel<bf16_t, 64>), grid, dim3(kBlock), 0, st, p);
         else hipLaunchKernelGGL((build_reps_kernel<bf16_t, 128>), grid, dim3(kBlock), 0, st, p);

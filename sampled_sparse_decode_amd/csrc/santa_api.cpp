@@ -159,6 +159,23 @@ santa_status santa_build_reps(const santa_kv *kv, void *reps, void *stream) {
     return launch_build_reps(p, stream);
 }
 
+santa_status santa_update_reps(const santa_kv *kv, void *reps, const int32_t *prev_seq_lens,
+                               int32_t max_new_tokens, void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!reps || !prev_seq_lens) return SANTA_ERR_NULL;
+    if (max_new_tokens < 0) return SANTA_ERR_SHAPE;
+    if (max_new_tokens == 0) return SANTA_OK;
+    Params p = base_params(*kv, nullptr, nullptr, nullptr, nullptr);
+    p.reps_out = reps;
+    p.prev_lens = prev_seq_lens;
+    // Tokens [prev, prev + n) touch at most ceil(n / T) + 1 teams from the
+    // one holding token prev; never more than the table holds.
+    const int64_t teams = (int64_t(max_new_tokens) + kv->page_size - 1) / kv->page_size + 1;
+    p.update_teams = int32_t(std::min<int64_t>(teams, kv->max_pages_per_seq));
+    return launch_build_reps(p, stream);
+}
+
 static santa_status santa_params(const santa_kv *kv, const void *q, int32_t M, float *out, float *lse,
                                  void *workspace, size_t workspace_bytes, Params *p) {
     santa_status st = validate_kv(kv);

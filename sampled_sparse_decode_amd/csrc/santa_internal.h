@@ -59,6 +59,8 @@ struct Params {
     const int32_t *given_teams;
     const float *given_w;
     void *reps_out;
+    const int32_t *prev_lens;   // build_reps update mode: lengths before the append (NULL: rebuild all)
+    int32_t update_teams;       // update mode: teams refreshed per sequence at most
 };
 
 // santa_pack_pages arguments.

@@ -21,6 +21,7 @@ _DTYPES = {torch.float32: SANTA_F32, torch.bfloat16: SANTA_BF16}
 EXPORTED = (
     "santa_workspace_size",
     "santa_build_reps",
+    "santa_update_reps",
     "santa_decode_attention",
     "santa_select_teams",
     "santa_attend_selected",
@@ -75,6 +76,7 @@ def load():
     sigs = {
         "santa_workspace_size": (i32, [kvp, i32, ctypes.POINTER(sz)]),
         "santa_build_reps": (i32, [kvp, P, P]),
+        "santa_update_reps": (i32, [kvp, P, P, i32, P]),
         "santa_decode_attention": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P, sz, P]),
         "santa_select_teams": (i32, [kvp, P, P, i32, u64, u32, P, P, P, sz, P]),
         "santa_attend_selected": (i32, [kvp, P, i32, P, P, P, sz, P]),
@@ -206,6 +208,17 @@ def santa_build_reps(kv, reps=None):
                            device=kv.device)
     d = kv.desc()
     _check("santa_build_reps", load().santa_build_reps(ctypes.byref(d), _ptr(reps), _stream()))
+    return reps
+
+
+def santa_update_reps(kv, reps, prev_seq_lens, max_new_tokens):
+    """Refresh the representatives of the teams that received tokens since the
+    sequence lengths were ``prev_seq_lens`` (device int32 [B])."""
+    if prev_seq_lens.dtype != torch.int32 or tuple(prev_seq_lens.shape) != (kv.batch,):
+        raise ValueError("prev_seq_lens must be an int32 [B] tensor")
+    d = kv.desc()
+    _check("santa_update_reps", load().santa_update_reps(ctypes.byref(d), _ptr(reps), _ptr(prev_seq_lens),
+                                                        int(max_new_tokens), _stream()))
     return reps
 
 

@@ -145,3 +145,14 @@ def test_pack_pages_validation(lib):
     # not overlap any buffer; the two sources may
     assert call(ptrs=(a, b, F(a.value + 4096), d)) == SHAPE
     assert call(ptrs=(a, b, c, F(c.value + (1 << 20) - 2))) == SHAPE
+
+
+def test_update_reps_validation(lib):
+    """santa_update_reps checks its arguments on the host; 0 new tokens enqueues nothing."""
+    k = kv()
+    F = ctypes.c_void_p(FAKE)
+    assert lib.santa_update_reps(ctypes.byref(k), None, F, 1, None) == NULL
+    assert lib.santa_update_reps(ctypes.byref(k), F, None, 1, None) == NULL
+    assert lib.santa_update_reps(ctypes.byref(k), F, F, -1, None) == SHAPE
+    assert lib.santa_update_reps(ctypes.byref(k), F, F, 0, None) == OK
+    assert lib.santa_update_reps(ctypes.byref(kv(page_size=48)), F, F, 1, None) == UNSUP
