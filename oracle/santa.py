@@ -29,6 +29,17 @@ Readings taken where the pages leave a step open (each repeated where used):
   R7  draws are independent per query head; a KV head's G query heads share
       nothing but the cache.
   R8  an empty sequence (length 0) gives out = 0 and lse = -inf.
+  R9  alternative representatives ([EXP] section 三 step 2 lists mean,
+      medoid and random; the mean is the default). The medoid is the member
+      key with the smallest sum of Euclidean distances to all members of its
+      team; each distance is the correctly rounded square root of the
+      channel-ordered float64 sum of squared float64 differences, the n
+      distances of a member are added in member order, and ties go to the
+      lowest member index. The random representative is member
+      floor(x n / 2^32), x = word 0 of Philox4x32-10 with counter
+      (t, g, b, 0) and key (seed lo ^ 0x52455053, seed hi) (a key of its own,
+      so its stream is disjoint from the team draws'). Both are copies of a
+      cached key, so no rounding is involved.
 
 Parity pins (tests/test_oracle_pins.py): dense attention against torch's
 scaled_dot_product_attention; full coverage against dense; brute-force
@@ -93,6 +104,62 @@ def build_reps(k_pages, page_table, seq_lens, page_size, dtype, seqs=None):
                 for c in range(d):
                     reps[b, t, g, c] = math.fsum(keys[g, :, c]) / n
             reps[b, t] = round_to_dtype(reps[b, t], dtype)
+    return reps
+
+
+REP_MEAN, REP_MEDOID, REP_RANDOM = 0, 1, 2
+REP_KEY_XOR = 0x52455053     # separates the random-representative stream from the draws (R9)
+
+
+def team_medoid_index(keys):
+    """Medoid of a team's keys [n][d] (float64 values of cached keys), reading R9.
+
+    [EXP] section 三 step 2 names the medoid as a representative choice: the
+    member whose distances to all members have the smallest sum. The loops
+    fix R9's orders (channels inside a distance, members across distances)
+    and run over all (i, j) pairs at once; np.sqrt is correctly rounded;
+    np.argmin takes the first (lowest) index among equal sums.
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    n, d = keys.shape
+    s2 = np.zeros((n, n))
+    for c in range(d):
+        diff = keys[:, None, c] - keys[None, :, c]              # [i][j]
+        s2 = s2 + diff * diff
+    dist = np.sqrt(s2)
+    total = np.zeros(n)
+    for j in range(n):
+        total = total + dist[:, j]
+    return int(np.argmin(total))
+
+
+def team_random_index(n, seed, b, t, g):
+    """Random member of a team of n keys (reading R9): floor(x n / 2^32)."""
+    from .philox import philox4x32_10, MASK32
+    seed = int(seed)
+    x = philox4x32_10((t, g, b, 0), ((seed & MASK32) ^ REP_KEY_XOR, (seed >> 32) & MASK32))[0]
+    return (x * n) >> 32
+
+
+def build_reps_kind(k_pages, page_table, seq_lens, page_size, dtype, kind, seed=0, seqs=None):
+    """Representatives of every team for kind REP_MEAN (build_reps), REP_MEDOID
+    or REP_RANDOM (R9); same layout and NaN convention as build_reps."""
+    if kind == REP_MEAN:
+        return build_reps(k_pages, page_table, seq_lens, page_size, dtype, seqs)
+    _, hkv, T, d = k_pages.shape
+    B, P = np.asarray(page_table).shape
+    reps = np.full((B, P, hkv, d), np.nan)
+    for b in range(B):
+        if seqs is not None and b not in seqs:
+            continue
+        L = int(seq_lens[b])
+        for t in range(num_teams(L, T)):
+            p = int(page_table[b][t])
+            n = team_size(L, T, t)
+            keys = decode(k_pages[p, :, :n, :], dtype)          # [Hkv][n][d]
+            for g in range(hkv):
+                i = team_medoid_index(keys[g]) if kind == REP_MEDOID else team_random_index(n, seed, b, t, g)
+                reps[b, t, g] = keys[g, i]
     return reps
 
 

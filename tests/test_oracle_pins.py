@@ -353,3 +353,91 @@ def test_union_size_closed_form():
                 u.add(santa.inverse_cdf(philox.word_to_uniform(x), e, C, Z))
         sizes[r] = len(u)
     assert abs(sizes.mean() - santa.expected_union_size(ps, M)) < 5 * sizes.std() / math.sqrt(R)
+
+
+# --------------------------------------------------------------------------
+# Alternative representatives: medoid and random member (reading R9)
+# --------------------------------------------------------------------------
+
+def test_medoid_of_collinear_keys_is_the_median():
+    # Points x_i * u on one line: the sum of distances |x_i - x_j| ||u|| is
+    # smallest at the median of the x_i (odd count: unique).
+    rng = np.random.default_rng(40)
+    u = np.zeros(32)
+    u[[0, 5, 17]] = [1.0, -2.0, 0.5]
+    for n in (3, 5, 9, 31):
+        x = rng.permutation(np.arange(n) * 3 - 20).astype(np.float64)
+        x[:] = x + rng.integers(0, 2, n)                     # uneven gaps, still distinct
+        keys = x[:, None] * u[None, :]
+        assert santa.team_medoid_index(keys) == int(np.argsort(x)[n // 2])
+    # Skewed: the median (member 4, x = 2) is not the point nearest the mean
+    # (member 0, x = 50), which summed squared distances would pick.
+    x = np.array([50.0, 100.0, 0.0, 1.0, 2.0])
+    assert santa.team_medoid_index(x[:, None] * u[None, :]) == 4
+
+
+def test_medoid_matches_scipy_distance_sums():
+    from scipy.spatial.distance import cdist
+    rng = np.random.default_rng(41)
+    for n, d in ((16, 64), (37, 128), (128, 64)):
+        keys = numerics.round_to_dtype(rng.standard_normal((n, d)) * 2.0, "bf16")
+        sums = cdist(keys, keys).sum(axis=1)
+        order = np.argsort(sums)
+        assert sums[order[1]] - sums[order[0]] > 1e-9 * sums[order[0]]   # no near tie in this sample
+        assert santa.team_medoid_index(keys) == int(order[0])
+
+
+def test_medoid_ties_go_to_the_lowest_index():
+    rng = np.random.default_rng(42)
+    k = rng.standard_normal((1, 16))
+    assert santa.team_medoid_index(np.repeat(k, 6, axis=0)) == 0             # all equal
+    assert santa.team_medoid_index(rng.standard_normal((2, 16))) == 0       # two keys: equal sums
+    assert santa.team_medoid_index(k) == 0                                  # a team of one
+    # The median point of a line, present twice (members 2 and 4): both have
+    # the smallest sum, member 2 is taken.
+    x = np.array([5.0, -3.0, 1.0, 9.0, 1.0, -7.0, 4.0])
+    assert santa.team_medoid_index(x[:, None] * np.ones((1, 8))) == 2
+
+
+def test_medoid_ignores_translation_and_never_takes_an_outlier():
+    rng = np.random.default_rng(43)
+    keys = np.round(rng.standard_normal((12, 16)) * 8)                       # small integers: exact
+    i = santa.team_medoid_index(keys)
+    assert santa.team_medoid_index(keys + 64.0) == i
+    far = keys.copy()
+    far[5] += 1e4
+    assert santa.team_medoid_index(far) != 5
+
+
+def test_random_member_is_uniform_and_in_range():
+    # Over many teams the chosen member of a team of n is uniform on 0..n-1.
+    from scipy.stats import chisquare
+    for n in (16, 5, 1):
+        idx = np.array([santa.team_random_index(n, 99, b, t, g)
+                        for b in range(4) for t in range(256) for g in range(4)])
+        assert idx.min() >= 0 and idx.max() < n
+        if n > 1:
+            counts = np.bincount(idx, minlength=n)
+            assert chisquare(counts).pvalue > 1e-4
+    # Its stream is not the draws': for one (b, team = draw block) the words differ.
+    assert [santa.team_random_index(2 ** 16, 7, 0, t, 0) for t in range(4)] != \
+        [(philox.philox4x32_10((t, 0, 0, 0), (7, 0))[0] * 2 ** 16) >> 32 for t in range(4)]
+
+
+def test_build_reps_kind_rows_are_team_members():
+    w = wl.paged_ragged(num_seqs=3, len_min=40, len_max=150, T=16, M=4, hq=4, hkv=2, d=32, dtype="bf16")
+    mean = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    assert np.array_equal(santa.build_reps_kind(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype,
+                                                santa.REP_MEAN), mean, equal_nan=True)
+    kd = numerics.decode(w.k_pages, w.dtype)
+    for kind in (santa.REP_MEDOID, santa.REP_RANDOM):
+        reps = santa.build_reps_kind(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype, kind, seed=3)
+        for b in range(w.batch):
+            L = int(w.seq_lens[b])
+            for t in range(santa.num_teams(L, w.page_size)):
+                n = santa.team_size(L, w.page_size, t)
+                tile = kd[int(w.page_table[b][t])]
+                for g in range(w.num_kv_heads):
+                    hits = np.all(tile[g, :n] == reps[b, t, g][None, :], axis=1)
+                    assert hits.any(), (kind, b, t, g)
+            assert np.all(np.isnan(reps[b, santa.num_teams(L, w.page_size):]))
