@@ -128,6 +128,14 @@ santa_status santa_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes);
  * Run once after prefill, and for a team again after its keys change. */
 santa_status santa_build_reps(const santa_kv *kv, void *reps, void *stream);
 
+/* Representative kinds of santa_build_reps_ex ([EXP] section 三 step 2 lists
+ * the mean, the medoid and a random member as choices of representative). */
+typedef enum santa_rep_kind {
+    SANTA_REP_MEAN = 0,         /* the rounded team mean (santa_build_reps)           */
+    SANTA_REP_MEDOID = 1,       /* the member nearest, in summed distance, to all      */
+    SANTA_REP_RANDOM = 2        /* a member drawn from a Philox stream of its own      */
+} santa_rep_kind;
+
 /* Representative upkeep after an append ([EXP] section 三 step 2: one
  * representative per team, here kept equal to the team mean as tokens
  * arrive). For each sequence b, recomputes reps[b][t] for the teams that
@@ -143,6 +151,30 @@ santa_status santa_build_reps(const santa_kv *kv, void *reps, void *stream);
  *                  (>= 0; 0 enqueues nothing) */
 santa_status santa_update_reps(const santa_kv *kv, void *reps, const int32_t *prev_seq_lens,
                                int32_t max_new_tokens, void *stream);
+
+/* Representatives of another kind ([EXP] section 三 step 2: mean, medoid or
+ * random member), built for every team or refreshed after an append.
+ *   kind            SANTA_REP_MEAN: exactly santa_build_reps (or, with
+ *                   prev_seq_lens, santa_update_reps).
+ *                   SANTA_REP_MEDOID: the member key k_i of the team's n keys
+ *                   minimising sum_j ||k_i - k_j||, copied exactly. Each
+ *                   distance is the correctly rounded float64 square root of
+ *                   the float64 sum, in channel order, of the squared float64
+ *                   channel differences; a member's n distances are added in
+ *                   member order; equal sums go to the lower member index.
+ *                   Costs n * n * d float64 multiply-adds per team and head.
+ *                   SANTA_REP_RANDOM: member floor(x * n / 2^32), x = word 0
+ *                   of Philox4x32-10 with counter (t, g, b, 0) and key
+ *                   (seed lo ^ 0x52455053, seed hi), copied exactly.
+ *   seed            SANTA_REP_RANDOM only; the key word change keeps this
+ *                   stream apart from the team draws of the same seed
+ *   prev_seq_lens   NULL: rows of every team t < K_b are written. Else the
+ *                   update mode of santa_update_reps (same meaning of
+ *                   prev_seq_lens and max_new_tokens), with the same result
+ *                   as a full build of this kind.
+ * Returns SANTA_ERR_SHAPE for another kind or a negative max_new_tokens. */
+santa_status santa_build_reps_ex(const santa_kv *kv, void *reps, int32_t kind, uint64_t seed,
+                                 const int32_t *prev_seq_lens, int32_t max_new_tokens, void *stream);
 
 /* SANTA++ decode attention ([ABS]; [EXP] section 三 steps 2-7).
  * For each sequence b and query head h (KV head g):

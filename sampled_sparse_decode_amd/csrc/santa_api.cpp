@@ -176,6 +176,27 @@ santa_status santa_update_reps(const santa_kv *kv, void *reps, const int32_t *pr
     return launch_build_reps(p, stream);
 }
 
+santa_status santa_build_reps_ex(const santa_kv *kv, void *reps, int32_t kind, uint64_t seed,
+                                 const int32_t *prev_seq_lens, int32_t max_new_tokens, void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!reps) return SANTA_ERR_NULL;
+    if (kind != SANTA_REP_MEAN && kind != SANTA_REP_MEDOID && kind != SANTA_REP_RANDOM) return SANTA_ERR_SHAPE;
+    Params p = base_params(*kv, nullptr, nullptr, nullptr, nullptr);
+    p.reps_out = reps;
+    p.rep_kind = kind;
+    p.seed_lo = uint32_t(seed);
+    p.seed_hi = uint32_t(seed >> 32);
+    if (prev_seq_lens) {
+        if (max_new_tokens < 0) return SANTA_ERR_SHAPE;
+        if (max_new_tokens == 0) return SANTA_OK;
+        p.prev_lens = prev_seq_lens;
+        const int64_t teams = (int64_t(max_new_tokens) + kv->page_size - 1) / kv->page_size + 1;
+        p.update_teams = int32_t(std::min<int64_t>(teams, kv->max_pages_per_seq));
+    }
+    return launch_build_reps(p, stream);
+}
+
 static santa_status santa_params(const santa_kv *kv, const void *q, int32_t M, float *out, float *lse,
                                  void *workspace, size_t workspace_bytes, Params *p) {
     santa_status st = validate_kv(kv);
@@ -300,6 +321,6 @@ const char *santa_status_string(int32_t status) {
     }
 }
 
-int32_t santa_version(void) { return 200; }
+int32_t santa_version(void) { return 210; }
 
 }  // extern "C"

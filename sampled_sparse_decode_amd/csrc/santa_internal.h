@@ -61,7 +61,10 @@ struct Params {
     void *reps_out;
     const int32_t *prev_lens;   // build_reps update mode: lengths before the append (NULL: rebuild all)
     int32_t update_teams;       // update mode: teams refreshed per sequence at most
+    int32_t rep_kind;           // santa_rep_kind of build_reps launches (seed_lo/hi key the random kind)
 };
+
+constexpr uint32_t kRepKeyXor = 0x52455053u;   // random representatives: key word 0 = seed lo ^ this
 
 // santa_pack_pages arguments.
 struct PackParams {

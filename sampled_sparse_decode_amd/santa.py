@@ -22,6 +22,7 @@ EXPORTED = (
     "santa_workspace_size",
     "santa_build_reps",
     "santa_update_reps",
+    "santa_build_reps_ex",
     "santa_decode_attention",
     "santa_select_teams",
     "santa_attend_selected",
@@ -77,6 +78,7 @@ def load():
         "santa_workspace_size": (i32, [kvp, i32, ctypes.POINTER(sz)]),
         "santa_build_reps": (i32, [kvp, P, P]),
         "santa_update_reps": (i32, [kvp, P, P, i32, P]),
+        "santa_build_reps_ex": (i32, [kvp, P, i32, u64, P, i32, P]),
         "santa_decode_attention": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P, sz, P]),
         "santa_select_teams": (i32, [kvp, P, P, i32, u64, u32, P, P, P, sz, P]),
         "santa_attend_selected": (i32, [kvp, P, i32, P, P, P, sz, P]),
@@ -219,6 +221,31 @@ def santa_update_reps(kv, reps, prev_seq_lens, max_new_tokens):
     d = kv.desc()
     _check("santa_update_reps", load().santa_update_reps(ctypes.byref(d), _ptr(reps), _ptr(prev_seq_lens),
                                                         int(max_new_tokens), _stream()))
+    return reps
+
+
+REP_MEAN, REP_MEDOID, REP_RANDOM = 0, 1, 2
+_REP_KINDS = {"mean": REP_MEAN, "medoid": REP_MEDOID, "random": REP_RANDOM}
+
+
+def santa_build_reps_ex(kv, kind, reps=None, seed=0, prev_seq_lens=None, max_new_tokens=0):
+    """Representatives of kind "mean", "medoid" or "random" (or its integer
+    code): [B][P][Hkv][d]. With ``prev_seq_lens`` only the teams that received
+    tokens since those lengths are refreshed, as in santa_update_reps."""
+    code = _REP_KINDS.get(kind, kind) if isinstance(kind, str) else int(kind)
+    if isinstance(code, str):
+        raise ValueError(f"unknown representative kind {kind!r}")
+    if reps is None:
+        reps = torch.zeros((kv.batch, kv.max_pages_per_seq, kv.num_kv_heads, kv.head_dim), dtype=kv.dtype,
+                           device=kv.device)
+    if prev_seq_lens is not None and (prev_seq_lens.dtype != torch.int32
+                                      or tuple(prev_seq_lens.shape) != (kv.batch,)):
+        raise ValueError("prev_seq_lens must be an int32 [B] tensor")
+    d = kv.desc()
+    _check("santa_build_reps_ex",
+           load().santa_build_reps_ex(ctypes.byref(d), _ptr(reps), code, int(seed) & (2**64 - 1),
+                                      _ptr(prev_seq_lens) if prev_seq_lens is not None else None,
+                                      int(max_new_tokens), _stream()))
     return reps
 
 

@@ -46,7 +46,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.santa_version() == 200
+    assert lib.santa_version() == 210
     for code in range(6):
         assert S.santa_status_string(code)
     assert S.santa_status_string(99) == "unknown status"
@@ -156,3 +156,18 @@ def test_update_reps_validation(lib):
     assert lib.santa_update_reps(ctypes.byref(k), F, F, -1, None) == SHAPE
     assert lib.santa_update_reps(ctypes.byref(k), F, F, 0, None) == OK
     assert lib.santa_update_reps(ctypes.byref(kv(page_size=48)), F, F, 1, None) == UNSUP
+
+
+def test_build_reps_ex_validation(lib):
+    """santa_build_reps_ex: unknown kinds and bad update bounds are rejected
+    on the host; an update with 0 new tokens enqueues nothing."""
+    k = kv()
+    F = ctypes.c_void_p(FAKE)
+    assert lib.santa_build_reps_ex(ctypes.byref(k), None, 1, 0, None, 0, None) == NULL
+    assert lib.santa_build_reps_ex(ctypes.byref(k), F, 3, 0, None, 0, None) == SHAPE
+    assert lib.santa_build_reps_ex(ctypes.byref(k), F, -1, 0, None, 0, None) == SHAPE
+    assert lib.santa_build_reps_ex(ctypes.byref(k), F, 2, 0, F, -1, None) == SHAPE
+    assert lib.santa_build_reps_ex(ctypes.byref(k), F, 1, 0, F, 0, None) == OK
+    assert lib.santa_build_reps_ex(ctypes.byref(kv(head_dim=96)), F, 1, 0, None, 0, None) == UNSUP
+    with pytest.raises(ValueError):
+        S.santa_build_reps_ex(None, "centroid")
