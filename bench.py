@@ -251,6 +251,26 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False):
         S.santa_select_teams(cache[j], q, reps[j], M, w.seed, w.offset, wss[j])
     torch.cuda.synchronize()
     r["attend_us"], _ = median_graph(attend_step, R, steps, warmup, torch)
+
+    # Representative upkeep of one decode step: every sequence's last token is
+    # taken as just appended (lengths one less before), its team refreshed.
+    prev = (kv0.seq_lens - 1).clamp(min=0)
+
+    def update_step(i):
+        j = i % R
+        S.santa_update_reps(cache[j], reps[j], prev, 1)
+
+    r["update_reps_us"], _ = median_graph(update_step, R, steps, warmup, torch)
+
+    # A full build of each kind of representative over one layer's cache (the
+    # cost after prefill), into a scratch buffer so the decode reps stay.
+    scratch = torch.empty_like(reps[0])
+    r["build_reps_us"] = {}
+    for kind in ("mean", "medoid", "random"):
+        def build_step(i, kind=kind):
+            S.santa_build_reps_ex(cache[i % R], kind, reps=scratch, seed=1)
+
+        r["build_reps_us"][kind], _ = median_graph(build_step, R, max(R, steps // 4), warmup // 4, torch)
     if calibrate:
         # Plain device copies of a known size, so rocprofv3 FETCH_SIZE / WRITE_SIZE
         # counters can be scaled (bytes per counter unit).
@@ -310,6 +330,8 @@ def main():
                   "bytes": ab["dense"]},
         "speedup_vs_dense": round(dense_us / santa_us, 3),
         "kv_read_fraction": {"per_query_head": round(ab["frac_head"], 4), "hbm": round(ab["frac_hbm"], 4)},
+        "update_reps_us": round(r["update_reps_us"], 3),
+        "build_reps_us": {k: round(v, 2) for k, v in r["build_reps_us"].items()},
         "roofline": {"kernel": "gather+combine (santa_attend_selected)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
@@ -327,7 +349,8 @@ def main():
                        "attend_us": round(rs["attend_us"], 2),
                        "attend_frac_of_peak": round(gbps(a["attend"], rs["attend_us"]) / HBM_PEAK_GBPS, 4),
                        "dense_frac_of_peak": round(gbps(a["dense"], rs["dense_us"]) / HBM_PEAK_GBPS, 4),
-                       "kv_read_fraction_hbm": round(a["frac_hbm"], 4)}
+                       "kv_read_fraction_hbm": round(a["frac_hbm"], 4),
+                       "build_reps_us": {k: round(v, 2) for k, v in rs["build_reps_us"].items()}}
         del ws
         torch.cuda.empty_cache()
     if scale:
