@@ -40,6 +40,18 @@ Readings taken where the pages leave a step open (each repeated where used):
       (t, g, b, 0) and key (seed lo ^ 0x52455053, seed hi) (a key of its own,
       so its stream is disjoint from the team draws'). Both are copies of a
       cached key, so no rounding is involved.
+  R10 variance-reduced team draws (the SANTA page, "Stochastic Sparse
+      Attention for Memory-Bound Inference", abstract: stratified and
+      systematic sampling lower the estimator's variance; here applied to the
+      team draw). The M points u_j that pick teams through the same inverse
+      CDF are, for the systematic scheme, (j + u0) / M with one uniform u0
+      (word 0 of the block with counter (0, h, b, offset)), and for the
+      stratified scheme (j + U_j) / M with U_j the uniform of draw j of the
+      independent scheme. In units of 1/M team t covers [a, a + w) with
+      a = M C_(t-1) / Z and w = M p_t; its inclusion probability is
+      min(1, w) (systematic: the points are one unit apart) and
+      1 - prod_j (1 - |[a, a + w) n [j, j + 1)|) (stratified: one
+      independent point per unit). Full coverage (R6) is unchanged.
 
 Parity pins (tests/test_oracle_pins.py): dense attention against torch's
 scaled_dot_product_attention; full coverage against dense; brute-force
@@ -50,6 +62,7 @@ against p; invariants (constant values, permuted page tables); team scores
 with one-token teams against the attention weights of the library routine.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -216,6 +229,50 @@ def draw_distance_to_boundary(u, C, Z):
     return float(np.min(np.abs(u - C[:-1] / Z)))
 
 
+DRAW_IID, DRAW_SYSTEMATIC, DRAW_STRATIFIED = 0, 1, 2
+
+
+def draw_uniforms(scheme, M, seed, offset, b, h):
+    """The M points in (0, 1) that pick one head's teams (R4; R10).
+
+    Independent: u_j from draw j's Philox word. Systematic: (j + u0) / M,
+    u0 the first of those uniforms. Stratified: (j + u_j) / M. The sums
+    j + u are exact in float64 (u has 33 significant bits) and the division
+    is correctly rounded.
+    """
+    u = [word_to_uniform(x) for x in draw_words(M, seed, offset, b, h)]
+    if scheme == DRAW_IID:
+        return u
+    if scheme == DRAW_SYSTEMATIC:
+        return [(j + u[0]) / M for j in range(M)]
+    if scheme == DRAW_STRATIFIED:
+        return [(j + u[j]) / M for j in range(M)]
+    raise ValueError(f"unknown draw scheme {scheme!r}")
+
+
+def inclusion_probability_scheme(scheme, t, C, Z, p, M):
+    """Inclusion probability of team t under a draw scheme (R4; R10).
+
+    For the stratified scheme the product over units is evaluated exactly in
+    rational arithmetic on the float64 values a = M C_(t-1) / Z and
+    w = M p_t, then rounded once.
+    """
+    if scheme == DRAW_IID:
+        return inclusion_probability(p[t], M)
+    if scheme == DRAW_SYSTEMATIC:
+        return min(1.0, M * p[t])
+    if scheme != DRAW_STRATIFIED:
+        raise ValueError(f"unknown draw scheme {scheme!r}")
+    a = Fraction(M * C[t - 1] / Z) if t > 0 else Fraction(0)
+    end = a + Fraction(M) * Fraction(p[t])
+    miss = Fraction(1)
+    for j in range(max(0, math.floor(a)), min(M, math.ceil(end))):
+        overlap = min(end, Fraction(j + 1)) - max(a, Fraction(j))
+        if overlap > 0:
+            miss *= 1 - overlap
+    return float(1 - miss)
+
+
 def inclusion_probability(p, M):
     """pi = 1 - (1 - p)^M, computed as -expm1(M * log1p(-p)) (R4).
 
@@ -242,13 +299,13 @@ class Selection:
         return [1.0 / x for x in self.pi]
 
 
-def select_teams(q_h, rep_rows, M, seed, offset, b, h):
-    """Sample teams for one query head (steps 2-3 of [EXP] section 三; [ABS]; R4, R6, R7).
+def select_teams(q_h, rep_rows, M, seed, offset, b, h, scheme=DRAW_IID):
+    """Sample teams for one query head (steps 2-3 of [EXP] section 三; [ABS]; R4, R6, R7, R10).
 
-    Draw j uses uniform u_j from Philox4x32-10 (see oracle/philox.py for the
-    counter layout) and takes team inverse_cdf(u_j). Draws whose uniform lies
-    within NEAR_TIE of a CDF boundary are recorded: both neighbouring teams
-    are listed in near_tie_teams.
+    Draw j uses point u_j of draw_uniforms (Philox4x32-10; see oracle/philox.py
+    for the counter layout) and takes team inverse_cdf(u_j). Draws whose
+    point lies within NEAR_TIE of a CDF boundary are recorded: both
+    neighbouring teams are listed in near_tie_teams.
     """
     K = len(rep_rows)
     s = rep_scores(q_h, rep_rows)
@@ -258,15 +315,14 @@ def select_teams(q_h, rep_rows, M, seed, offset, b, h):
         return Selection(teams, [1.0] * K, p, set(), [], True)
     near = set()
     draws = []
-    for x in draw_words(M, seed, offset, b, h):
-        u = word_to_uniform(x)
+    for u in draw_uniforms(scheme, M, seed, offset, b, h):
         t = inverse_cdf(u, e, C, Z)
         draws.append(t)
         if draw_distance_to_boundary(u, C, Z) < NEAR_TIE:
             k = int(np.argmin(np.abs(u - C[:-1] / Z)))
             near.update((k, k + 1))
     teams = sorted(set(draws))
-    pi = [inclusion_probability(p[t], M) for t in teams]
+    pi = [inclusion_probability_scheme(scheme, t, C, Z, p, M) for t in teams]
     return Selection(teams, pi, p, near, draws, False)
 
 
@@ -374,7 +430,7 @@ class HeadResult:
         self.out, self.lse, self.selection = out, lse, selection
 
 
-def santa_head(kv, q_h, reps, b, h, num_q_heads, M, seed, offset):
+def santa_head(kv, q_h, reps, b, h, num_q_heads, M, seed, offset, scheme=DRAW_IID):
     """SANTA++ for one (sequence b, query head h): select teams, then estimate.
 
     q_h: float64 query [d]; reps: float64 [B][max_pages][Hkv][d] (from build_reps).
@@ -386,7 +442,7 @@ def santa_head(kv, q_h, reps, b, h, num_q_heads, M, seed, offset):
     if K == 0:
         return HeadResult(np.zeros(kv.d), -math.inf, Selection([], [], np.zeros(0), set(), [], True))
     rep_rows = np.stack([reps[b, t, g] for t in range(K)])
-    sel = select_teams(q_h, rep_rows, M, seed, offset, b, h)
+    sel = select_teams(q_h, rep_rows, M, seed, offset, b, h, scheme)
     out, lse = estimate(q_h, [kv.team(b, g, t) for t in sel.teams], sel.inv_pi)
     return HeadResult(out, lse, sel)
 

@@ -441,3 +441,123 @@ def test_build_reps_kind_rows_are_team_members():
                     hits = np.all(tile[g, :n] == reps[b, t, g][None, :], axis=1)
                     assert hits.any(), (kind, b, t, g)
             assert np.all(np.isnan(reps[b, santa.num_teams(L, w.page_size):]))
+
+
+# --------------------------------------------------------------------------
+# Variance-reduced team draws: systematic and stratified (reading R10)
+# --------------------------------------------------------------------------
+
+def _team_probs(K, seed, spread=1.5):
+    s = list(np.random.default_rng(seed).standard_normal(K) * spread)
+    return santa.team_softmax(s)
+
+
+def test_scheme_points_layout():
+    for M in (1, 5, 31):
+        iid = santa.draw_uniforms(santa.DRAW_IID, M, 7, 3, 1, 2)
+        sys_ = santa.draw_uniforms(santa.DRAW_SYSTEMATIC, M, 7, 3, 1, 2)
+        strat = santa.draw_uniforms(santa.DRAW_STRATIFIED, M, 7, 3, 1, 2)
+        assert 0 < sys_[0] < 1 / M
+        assert np.allclose(np.diff(sys_), 1 / M, rtol=0, atol=1e-15)     # one unit apart
+        assert abs(sys_[0] * M - iid[0]) < 1e-15
+        for j in range(M):
+            assert j / M < strat[j] < (j + 1) / M                      # one point per unit
+            assert abs(strat[j] * M - j - iid[j]) < 1e-13
+
+
+def _pieces(breaks):
+    b = sorted(set([0.0, 1.0] + [x for x in breaks if 0.0 < x < 1.0]))
+    return zip(b[:-1], b[1:])
+
+
+def test_systematic_inclusion_by_exact_integration():
+    # With one uniform u0 the drawn set is piecewise constant in u0, changing
+    # only where a point (j + u0)/M crosses a boundary C_t/Z. Integrating the
+    # selection rule itself over the pieces gives P(t in S) exactly; it must
+    # equal min(1, M p_t), and the weighted team sums must be unbiased.
+    for K, M, seed in ((40, 8, 1), (17, 5, 2), (64, 31, 3)):
+        e, C, Z, p = _team_probs(K, seed)
+        X = np.random.default_rng(seed + 10).standard_normal(K)
+        pi = np.array([santa.inclusion_probability_scheme(santa.DRAW_SYSTEMATIC, t, C, Z, p, M)
+                       for t in range(K)])
+        incl = np.zeros(K)
+        ht = 0.0
+        for lo, hi in _pieces([(M * c / Z) % 1.0 for c in C]):
+            S = {santa.inverse_cdf((j + (lo + hi) / 2) / M, e, C, Z) for j in range(M)}
+            for t in S:
+                incl[t] += hi - lo
+                ht += (hi - lo) * X[t] / pi[t]
+        assert np.max(np.abs(incl - pi)) < 1e-12
+        assert abs(ht - X.sum()) < 1e-10 * np.abs(X).sum()
+        assert np.any((pi > 0.3) & (pi < 1.0)) and np.any(pi == 1.0)  # both regimes occur
+
+
+def test_stratified_inclusion_by_exact_integration():
+    # Stratum j's point is uniform on [j/M, (j+1)/M) and independent of the
+    # others: P(point j in t) is the measure of the piece of the stratum the
+    # selection rule sends to t, and P(t in S) = 1 - prod_j (1 - that).
+    for K, M, seed in ((40, 8, 4), (17, 5, 5), (64, 31, 6), (6, 4, 7)):
+        e, C, Z, p = _team_probs(K, seed)
+        hit = np.zeros((M, K))
+        for j in range(M):
+            for lo, hi in _pieces([M * c / Z - j for c in C]):
+                hit[j, santa.inverse_cdf((j + (lo + hi) / 2) / M, e, C, Z)] += hi - lo
+        brute = 1.0 - np.prod(1.0 - hit, axis=0)
+        pi = np.array([santa.inclusion_probability_scheme(santa.DRAW_STRATIFIED, t, C, Z, p, M)
+                       for t in range(K)])
+        assert np.max(np.abs(brute - pi)) < 1e-12
+        # It is neither the independent nor the systematic probability.
+        iid = np.array([santa.inclusion_probability(x, M) for x in p])
+        assert np.max(np.abs(pi - iid)) > 1e-3 and np.max(np.abs(pi - np.minimum(1, M * p))) > 1e-3
+
+
+def test_stratified_inclusion_of_tiny_teams_is_accurate():
+    # A team far narrower than a unit: pi = M p to full relative precision.
+    s = [0.0] * 10 + [-40.0] + [0.0] * 10
+    e, C, Z, p = santa.team_softmax(s)
+    for scheme in (santa.DRAW_SYSTEMATIC, santa.DRAW_STRATIFIED):
+        pi = santa.inclusion_probability_scheme(scheme, 10, C, Z, p, 7)
+        assert abs(pi / (7 * p[10]) - 1.0) < 1e-9
+
+
+def test_systematic_uniform_teams_draw_exactly_m():
+    # Equal team probabilities 1/K < 1/M: the points are one unit apart and
+    # every team is narrower than a unit, so M distinct teams every time.
+    K, M = 50, 12
+    e, C, Z, p = santa.team_softmax([0.0] * K)
+    for seed in range(50):
+        u = santa.draw_uniforms(santa.DRAW_SYSTEMATIC, M, seed, 0, 0, 0)
+        assert len({santa.inverse_cdf(x, e, C, Z) for x in u}) == M
+
+
+def test_variance_reduced_schemes_lower_the_error():
+    # Teams of keys around their own centre (so the representatives are
+    # informative, p close to each team's share of the softmax mass); many
+    # seeds: every scheme is unbiased in the denominator, and the systematic
+    # and stratified ones spread it, and the output error, clearly less than
+    # independent draws.
+    K, d, T, M = 32, 32, 16, 8
+    rng = np.random.default_rng(9)
+    mu = rng.standard_normal((K, d))
+    keys = (np.repeat(mu, T, axis=0) + 0.3 * rng.standard_normal((K * T, d))).astype(np.float32)[None, None]
+    vals = rng.standard_normal((1, 1, K * T, d)).astype(np.float32)
+    q = (2.0 * rng.standard_normal((1, 1, d))).astype(np.float32)
+    w = wl._contiguous("coherent_teams", "f32", keys, vals, q, T, M)
+    kv = _kv(w)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    qh = numerics.decode(w.q[0, 0], "f32")
+    out_d, lse_d = santa.dense_attention(qh, *kv.all_tokens(0, 0))
+    R = 600
+    sd, mse = {}, {}
+    for scheme in (santa.DRAW_IID, santa.DRAW_SYSTEMATIC, santa.DRAW_STRATIFIED):
+        Dr = np.empty(R)
+        err = np.empty(R)
+        for seed in range(R):
+            r = santa.santa_head(kv, qh, reps, 0, 0, 1, M, seed, 0, scheme)
+            Dr[seed] = math.exp(r.lse - lse_d)
+            err[seed] = np.sum((r.out - out_d) ** 2)
+        assert abs(Dr.mean() - 1.0) < 5 * Dr.std() / math.sqrt(R) + 1e-12
+        sd[scheme], mse[scheme] = Dr.std(), err.mean()
+    for scheme in (santa.DRAW_SYSTEMATIC, santa.DRAW_STRATIFIED):
+        assert sd[scheme] < 0.6 * sd[santa.DRAW_IID]
+        assert mse[scheme] < 0.75 * mse[santa.DRAW_IID]
