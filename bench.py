@@ -252,6 +252,24 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False):
     torch.cuda.synchronize()
     r["attend_us"], _ = median_graph(attend_step, R, steps, warmup, torch)
 
+    # The variance-reduced draw schemes: whole decode call, and the bytes of
+    # their (larger: fewer repeated teams) unions.
+    r["schemes"] = {}
+    for name in ("systematic", "stratified"):
+        _, _, smp, _ = S.santa_decode_attention_ex(kv0, q, reps[0], M, name, w.seed, w.offset, wss[0],
+                                                   return_sets=True)
+        torch.cuda.synchronize()
+        abs_ = algorithmic_bytes(w, union_stats(w, smp.cpu().numpy()))
+
+        def scheme_step(i, name=name):
+            j = i % R
+            S.santa_decode_attention_ex(cache[j], q, reps[j], M, name, w.seed, w.offset, wss[j], out, lse)
+
+        us, _ = median_graph(scheme_step, R, steps, warmup, torch)
+        r["schemes"][name] = {"us_per_layer": round(us, 3),
+                              "kv_read_fraction": {"per_query_head": round(abs_["frac_head"], 4),
+                                                   "hbm": round(abs_["frac_hbm"], 4)}}
+
     # Representative upkeep of one decode step: every sequence's last token is
     # taken as just appended (lengths one less before), its team refreshed.
     prev = (kv0.seq_lens - 1).clamp(min=0)
@@ -332,6 +350,7 @@ def main():
         "kv_read_fraction": {"per_query_head": round(ab["frac_head"], 4), "hbm": round(ab["frac_hbm"], 4)},
         "update_reps_us": round(r["update_reps_us"], 3),
         "build_reps_us": {k: round(v, 2) for k, v in r["build_reps_us"].items()},
+        "draw_schemes": r["schemes"],
         "roofline": {"kernel": "gather+combine (santa_attend_selected)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
@@ -350,7 +369,8 @@ def main():
                        "attend_frac_of_peak": round(gbps(a["attend"], rs["attend_us"]) / HBM_PEAK_GBPS, 4),
                        "dense_frac_of_peak": round(gbps(a["dense"], rs["dense_us"]) / HBM_PEAK_GBPS, 4),
                        "kv_read_fraction_hbm": round(a["frac_hbm"], 4),
-                       "build_reps_us": {k: round(v, 2) for k, v in rs["build_reps_us"].items()}}
+                       "build_reps_us": {k: round(v, 2) for k, v in rs["build_reps_us"].items()},
+                       "draw_schemes": rs["schemes"]}
         del ws
         torch.cuda.empty_cache()
     if scale:

@@ -207,6 +207,38 @@ santa_status santa_decode_attention(const santa_kv *kv, const void *q, const voi
                                     float *out, float *lse, int32_t *sampled, float *inv_pi,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Where the M draws of santa_decode_attention_ex / santa_select_teams_ex
+ * fall. The SANTA page ("Stochastic Sparse Attention for Memory-Bound
+ * Inference", abstract) introduces stratified and systematic sampling as
+ * lower-variance variants; here they place the team draws. Each scheme
+ * takes draw j's uniform u_j = (word + 1/2) 2^-32 as in step 3 of
+ * santa_decode_attention and sends a point through the same inverse CDF
+ * (first t with point * C_last < C_t):
+ *   SANTA_DRAW_IID         point u_j; pi = 1 - (1 - p)^M
+ *   SANTA_DRAW_SYSTEMATIC  point (j + u_0) / M; pi = min(1, M p)
+ *   SANTA_DRAW_STRATIFIED  point (j + u_j) / M; with a = M C_(t-1) / C_last
+ *                          and w = M p_t, q1 = min(w, floor(a) + 1 - a) and
+ *                          r = w - q1: pi = 1 if r >= 1, else w - q1 r
+ *                          (= 1 - (1 - q1)(1 - r))
+ * Every scheme keeps the full-coverage rule (M >= K_b: all teams, pi = 1). */
+typedef enum santa_draw_scheme {
+    SANTA_DRAW_IID = 0,
+    SANTA_DRAW_SYSTEMATIC = 1,
+    SANTA_DRAW_STRATIFIED = 2
+} santa_draw_scheme;
+
+/* santa_decode_attention and santa_select_teams with a draw scheme
+ * (santa_draw_scheme); SANTA_DRAW_IID gives exactly the plain calls.
+ * Returns SANTA_ERR_SHAPE for another scheme; otherwise as the plain calls. */
+santa_status santa_decode_attention_ex(const santa_kv *kv, const void *q, const void *reps,
+                                       int32_t M, uint64_t seed, uint32_t offset, int32_t scheme,
+                                       float *out, float *lse, int32_t *sampled, float *inv_pi,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+santa_status santa_select_teams_ex(const santa_kv *kv, const void *q, const void *reps,
+                                   int32_t M, uint64_t seed, uint32_t offset, int32_t scheme,
+                                   int32_t *sampled, float *inv_pi,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* The two stages of santa_decode_attention, for callers that time or
  * schedule them separately; running santa_select_teams and then
  * santa_attend_selected on the same workspace equals one

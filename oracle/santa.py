@@ -323,7 +323,9 @@ def select_teams(q_h, rep_rows, M, seed, offset, b, h, scheme=DRAW_IID):
             near.update((k, k + 1))
     teams = sorted(set(draws))
     pi = [inclusion_probability_scheme(scheme, t, C, Z, p, M) for t in teams]
-    return Selection(teams, pi, p, near, draws, False)
+    sel = Selection(teams, pi, p, near, draws, False)
+    sel.C, sel.Z = C, Z
+    return sel
 
 
 # ----------------------------------------------------------------------------

@@ -212,14 +212,17 @@ static santa_status santa_params(const santa_kv *kv, const void *q, int32_t M, f
     return SANTA_OK;
 }
 
-santa_status santa_select_teams(const santa_kv *kv, const void *q, const void *reps,
-                                int32_t M, uint64_t seed, uint32_t offset,
-                                int32_t *sampled, float *inv_pi,
-                                void *workspace, size_t workspace_bytes, void *stream) {
+santa_status santa_select_teams_ex(const santa_kv *kv, const void *q, const void *reps,
+                                   int32_t M, uint64_t seed, uint32_t offset, int32_t scheme,
+                                   int32_t *sampled, float *inv_pi,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
     Params p;
     santa_status st = santa_params(kv, q, M, nullptr, nullptr, workspace, workspace_bytes, &p);
     if (st != SANTA_OK) return st;
     if (!reps) return SANTA_ERR_NULL;
+    if (scheme != SANTA_DRAW_IID && scheme != SANTA_DRAW_SYSTEMATIC && scheme != SANTA_DRAW_STRATIFIED)
+        return SANTA_ERR_SHAPE;
+    p.scheme = scheme;
     if ((sampled == nullptr) != (inv_pi == nullptr)) return SANTA_ERR_NULL;
     p.reps = reps;
     p.seed_lo = uint32_t(seed & 0xffffffffu);
@@ -228,6 +231,14 @@ santa_status santa_select_teams(const santa_kv *kv, const void *q, const void *r
     p.sampled = sampled;
     p.inv_pi = inv_pi;
     return launch_select(p, stream);
+}
+
+santa_status santa_select_teams(const santa_kv *kv, const void *q, const void *reps,
+                                int32_t M, uint64_t seed, uint32_t offset,
+                                int32_t *sampled, float *inv_pi,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    return santa_select_teams_ex(kv, q, reps, M, seed, offset, SANTA_DRAW_IID, sampled, inv_pi,
+                                 workspace, workspace_bytes, stream);
 }
 
 santa_status santa_attend_selected(const santa_kv *kv, const void *q, int32_t M,
@@ -240,16 +251,25 @@ santa_status santa_attend_selected(const santa_kv *kv, const void *q, int32_t M,
     return run_gather_combine(p, stream);
 }
 
+santa_status santa_decode_attention_ex(const santa_kv *kv, const void *q, const void *reps,
+                                       int32_t M, uint64_t seed, uint32_t offset, int32_t scheme,
+                                       float *out, float *lse, int32_t *sampled, float *inv_pi,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!q || !reps || !out) return SANTA_ERR_NULL;
+    st = santa_select_teams_ex(kv, q, reps, M, seed, offset, scheme, sampled, inv_pi, workspace, workspace_bytes,
+                               stream);
+    if (st != SANTA_OK) return st;
+    return santa_attend_selected(kv, q, M, out, lse, workspace, workspace_bytes, stream);
+}
+
 santa_status santa_decode_attention(const santa_kv *kv, const void *q, const void *reps,
                                     int32_t M, uint64_t seed, uint32_t offset,
                                     float *out, float *lse, int32_t *sampled, float *inv_pi,
                                     void *workspace, size_t workspace_bytes, void *stream) {
-    santa_status st = validate_kv(kv);
-    if (st != SANTA_OK) return st;
-    if (!q || !reps || !out) return SANTA_ERR_NULL;
-    st = santa_select_teams(kv, q, reps, M, seed, offset, sampled, inv_pi, workspace, workspace_bytes, stream);
-    if (st != SANTA_OK) return st;
-    return santa_attend_selected(kv, q, M, out, lse, workspace, workspace_bytes, stream);
+    return santa_decode_attention_ex(kv, q, reps, M, seed, offset, SANTA_DRAW_IID, out, lse, sampled, inv_pi,
+                                     workspace, workspace_bytes, stream);
 }
 
 santa_status dense_decode_attention(const santa_kv *kv, const void *q, float *out, float *lse,
@@ -321,6 +341,6 @@ const char *santa_status_string(int32_t status) {
     }
 }
 
-int32_t santa_version(void) { return 210; }
+int32_t santa_version(void) { return 220; }
 
 }  // extern "C"

@@ -62,6 +62,7 @@ struct Params {
     const int32_t *prev_lens;   // build_reps update mode: lengths before the append (NULL: rebuild all)
     int32_t update_teams;       // update mode: teams refreshed per sequence at most
     int32_t rep_kind;           // santa_rep_kind of build_reps launches (seed_lo/hi key the random kind)
+    int32_t scheme;             // santa_draw_scheme of select launches
 };
 
 constexpr uint32_t kRepKeyXor = 0x52455053u;   // random representatives: key word 0 = seed lo ^ this

@@ -11,6 +11,9 @@
 //         sample M teams with probability p_i.
 //   [PHX] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
 //         1, 2, 3", SC'11 (Philox4x32-10).
+//   [SAN] "Stochastic Sparse Attention for Memory-Bound Inference" (the
+//         SANTA page), abstract: stratified and systematic sampling give
+//         lower-variance variants; here they place the team draws.
 //
 // Selection is decided in float64: products of two bfloat16 (or float32)
 // values are exact in float64 and the sums are accurate to ~1e-16, so a draw
@@ -151,20 +154,29 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     const bool full = K > 0 && p.M >= K;
 
     // 3. Wavefront 0 draws; the other wavefronts compute pi_t and log w_t for
-    //    every team meanwhile (pi = 1 - (1 - p)^M = -expm1(M log1p(-p))).
+    //    every team meanwhile.
     if (K > 0) {
         if (wave == 0) {
             if (full) {
                 for (int t = lane; t < K; t += 64) atomicOr(&bits_s[t >> 5], 1u << (t & 31));
             } else {
-                // M draws with replacement: u = (x + 1/2) 2^-32 from Philox word
-                // j mod 4 of counter (j / 4, h, b, offset); team = first t with
-                // u Z < C_t.
+                // Draw j's uniform: u_j = (x + 1/2) 2^-32 from Philox word
+                // j mod 4 of counter (j / 4, h, b, offset). Its point is u_j
+                // (independent draws), (j + u_0) / M (systematic) or
+                // (j + u_j) / M (stratified; [SAN]); team = first t with
+                // point * Z < C_t. j + u is exact in float64.
+                const uint4 r0 = philox4x32_10(make_uint4(0u, uint32_t(h), uint32_t(b), p.offset),
+                                               p.seed_lo, p.seed_hi);
+                const double u0 = (double(r0.x) + 0.5) * 0x1p-32;
                 for (int j = lane; j < p.M; j += 64) {
                     const uint4 r = philox4x32_10(make_uint4(uint32_t(j) >> 2, uint32_t(h), uint32_t(b), p.offset),
                                                   p.seed_lo, p.seed_hi);
                     const uint32_t x = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
-                    const double target = ((double(x) + 0.5) * 0x1p-32) * Z;
+                    const double uj = (double(x) + 0.5) * 0x1p-32;
+                    double point = uj;
+                    if (p.scheme == SANTA_DRAW_SYSTEMATIC) point = (double(j) + u0) / double(p.M);
+                    else if (p.scheme == SANTA_DRAW_STRATIFIED) point = (double(j) + uj) / double(p.M);
+                    const double target = point * Z;
                     int t;
                     if (target < Z) {
                         int w = 0;                      // first wavefront whose end exceeds the target
@@ -188,11 +200,35 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
                 }
             }
         } else {
+            // Inclusion probabilities. Independent: 1 - (1 - p)^M =
+            // -expm1(M log1p(-p)). Systematic: min(1, M p). Stratified: in
+            // units of 1/M the team covers [a, a + w), a = M C_(t-1) / Z,
+            // w = M p; it meets unit k = floor(a) over q1 = min(w, k + 1 - a)
+            // and the next units over r = w - q1, so pi = 1 if r >= 1 (a whole
+            // unit inside) else 1 - (1 - q1)(1 - r) = w - q1 r.
             for (int t = tid - 64; t < K; t += kSel - 64) {
                 double lw = 0.0, w = 1.0;
                 if (!full) {
                     const double pt_ = e_s[t] / Z;
-                    const double pi = -expm1(double(p.M) * log1p(-pt_));
+                    double pi;
+                    if (p.scheme == SANTA_DRAW_SYSTEMATIC) {
+                        pi = fmin(1.0, double(p.M) * pt_);
+                    } else if (p.scheme == SANTA_DRAW_STRATIFIED) {
+                        double cprev = 0.0;
+                        if (t > 0) {
+                            const int ww = (t - 1) / (64 * per);
+                            double bw = 0.0;
+                            for (int i = 0; i < ww; ++i) bw = wave_end(i, bw);
+                            cprev = bw + c_s[t - 1];
+                        }
+                        const double wd = double(p.M) * pt_;
+                        const double a = double(p.M) * cprev / Z;
+                        const double q1 = fmin(wd, (floor(a) + 1.0) - a);
+                        const double rest = wd - q1;
+                        pi = rest >= 1.0 ? 1.0 : wd - q1 * rest;
+                    } else {
+                        pi = -expm1(double(p.M) * log1p(-pt_));
+                    }
                     w = 1.0 / pi;
                     lw = -log(pi);
                 }

@@ -24,7 +24,9 @@ EXPORTED = (
     "santa_update_reps",
     "santa_build_reps_ex",
     "santa_decode_attention",
+    "santa_decode_attention_ex",
     "santa_select_teams",
+    "santa_select_teams_ex",
     "santa_attend_selected",
     "dense_decode_attention",
     "santa_attention_given_teams",
@@ -80,7 +82,9 @@ def load():
         "santa_update_reps": (i32, [kvp, P, P, i32, P]),
         "santa_build_reps_ex": (i32, [kvp, P, i32, u64, P, i32, P]),
         "santa_decode_attention": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P, sz, P]),
+        "santa_decode_attention_ex": (i32, [kvp, P, P, i32, u64, u32, i32, P, P, P, P, P, sz, P]),
         "santa_select_teams": (i32, [kvp, P, P, i32, u64, u32, P, P, P, sz, P]),
+        "santa_select_teams_ex": (i32, [kvp, P, P, i32, u64, u32, i32, P, P, P, sz, P]),
         "santa_attend_selected": (i32, [kvp, P, i32, P, P, P, sz, P]),
         "dense_decode_attention": (i32, [kvp, P, P, P, P, sz, P]),
         "santa_attention_given_teams": (i32, [kvp, P, i32, P, P, P, P, P, sz, P]),
@@ -254,9 +258,31 @@ def _check_q(kv, q):
         raise ValueError("q must be a contiguous [B][Hq][d] tensor of the cache dtype")
 
 
+DRAW_IID, DRAW_SYSTEMATIC, DRAW_STRATIFIED = 0, 1, 2
+_SCHEMES = {"iid": DRAW_IID, "systematic": DRAW_SYSTEMATIC, "stratified": DRAW_STRATIFIED}
+
+
+def _scheme_code(scheme):
+    if isinstance(scheme, str):
+        if scheme not in _SCHEMES:
+            raise ValueError(f"unknown draw scheme {scheme!r}")
+        return _SCHEMES[scheme]
+    return int(scheme)
+
+
 def santa_decode_attention(kv, q, reps, M, seed=0, offset=0, workspace=None, out=None, lse=None,
                            return_sets=False):
     """SANTA++ decode attention. Returns (out, lse) or (out, lse, sampled, inv_pi)."""
+    return _decode(kv, q, reps, M, seed, offset, None, workspace, out, lse, return_sets)
+
+
+def santa_decode_attention_ex(kv, q, reps, M, scheme, seed=0, offset=0, workspace=None, out=None, lse=None,
+                              return_sets=False):
+    """santa_decode_attention with a draw scheme: "iid", "systematic" or "stratified"."""
+    return _decode(kv, q, reps, M, seed, offset, _scheme_code(scheme), workspace, out, lse, return_sets)
+
+
+def _decode(kv, q, reps, M, seed, offset, scheme, workspace, out, lse, return_sets):
     _check_q(kv, q)
     B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
     dev = kv.device
@@ -271,10 +297,16 @@ def santa_decode_attention(kv, q, reps, M, seed=0, offset=0, workspace=None, out
         sampled = torch.empty((B, Hq, M), dtype=torch.int32, device=dev)
         inv_pi = torch.empty((B, Hq, M), dtype=torch.float32, device=dev)
     desc = kv.desc()
-    st = load().santa_decode_attention(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed), int(offset),
-                                       _ptr(out), _ptr(lse), _ptr(sampled), _ptr(inv_pi),
-                                       _ptr(workspace), workspace.numel(), _stream())
-    _check("santa_decode_attention", st)
+    if scheme is None:
+        st = load().santa_decode_attention(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed), int(offset),
+                                           _ptr(out), _ptr(lse), _ptr(sampled), _ptr(inv_pi),
+                                           _ptr(workspace), workspace.numel(), _stream())
+        _check("santa_decode_attention", st)
+    else:
+        st = load().santa_decode_attention_ex(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed),
+                                              int(offset), scheme, _ptr(out), _ptr(lse), _ptr(sampled),
+                                              _ptr(inv_pi), _ptr(workspace), workspace.numel(), _stream())
+        _check("santa_decode_attention_ex", st)
     if return_sets:
         return out, lse, sampled, inv_pi
     return out, lse
@@ -287,6 +319,16 @@ def santa_select_teams(kv, q, reps, M, seed, offset, workspace, sampled=None, in
     st = load().santa_select_teams(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed), int(offset),
                                    _ptr(sampled), _ptr(inv_pi), _ptr(workspace), workspace.numel(), _stream())
     _check("santa_select_teams", st)
+
+
+def santa_select_teams_ex(kv, q, reps, M, scheme, seed, offset, workspace, sampled=None, inv_pi=None):
+    """santa_select_teams with a draw scheme: "iid", "systematic" or "stratified"."""
+    _check_q(kv, q)
+    desc = kv.desc()
+    st = load().santa_select_teams_ex(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed), int(offset),
+                                      _scheme_code(scheme), _ptr(sampled), _ptr(inv_pi), _ptr(workspace),
+                                      workspace.numel(), _stream())
+    _check("santa_select_teams_ex", st)
 
 
 def santa_attend_selected(kv, q, M, workspace, out, lse=None):

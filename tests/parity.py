@@ -62,7 +62,8 @@ def _check_lse(w, got, ref, b, h):
         assert abs(got - ref) <= LSE_TOL[w.dtype] * max(1.0, abs(ref) / 16), f"(b={b}, h={h}) lse {got} vs {ref}"
 
 
-def check_santa_head(w, kv, reps, b, h, out, lse, teams, inv_pi, M=None, seed=None, offset=None):
+def check_santa_head(w, kv, reps, b, h, out, lse, teams, inv_pi, M=None, seed=None, offset=None,
+                     scheme=santa.DRAW_IID):
     """Compare one head's HIP sets, weights, output and lse with the oracle.
 
     Returns (max-abs error, near_tie_flip: bool).
@@ -71,7 +72,7 @@ def check_santa_head(w, kv, reps, b, h, out, lse, teams, inv_pi, M=None, seed=No
     seed = w.seed if seed is None else seed
     offset = w.offset if offset is None else offset
     qh = numerics.decode(w.q[b, h], w.dtype)
-    res = santa.santa_head(kv, qh, reps, b, h, w.num_q_heads, M, seed, offset)
+    res = santa.santa_head(kv, qh, reps, b, h, w.num_q_heads, M, seed, offset, scheme)
     sel = res.selection
     got_teams = [int(t) for t in teams if t >= 0]
     assert all(t < 0 for t in teams[len(got_teams):]), "sampled list not -1 padded"
@@ -85,7 +86,7 @@ def check_santa_head(w, kv, reps, b, h, out, lse, teams, inv_pi, M=None, seed=No
     if sel.full:
         ref_w = [1.0] * len(got_teams)
     else:
-        ref_w = [1.0 / santa.inclusion_probability(sel.p[t], M) for t in got_teams]
+        ref_w = [1.0 / santa.inclusion_probability_scheme(scheme, t, sel.C, sel.Z, sel.p, M) for t in got_teams]
     w_got = np.asarray(inv_pi[:len(got_teams)], dtype=np.float64)
     assert np.all(np.abs(w_got - ref_w) <= INV_PI_RTOL * np.abs(ref_w) + 1e-30), f"(b={b}, h={h}) 1/pi differs"
     assert np.all(np.asarray(inv_pi[len(got_teams):]) == 0.0)

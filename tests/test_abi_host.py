@@ -46,7 +46,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.santa_version() == 210
+    assert lib.santa_version() == 220
     for code in range(6):
         assert S.santa_status_string(code)
     assert S.santa_status_string(99) == "unknown status"
@@ -171,3 +171,19 @@ def test_build_reps_ex_validation(lib):
     assert lib.santa_build_reps_ex(ctypes.byref(kv(head_dim=96)), F, 1, 0, None, 0, None) == UNSUP
     with pytest.raises(ValueError):
         S.santa_build_reps_ex(None, "centroid")
+
+
+def test_draw_scheme_validation(lib):
+    """The _ex entry points reject unknown draw schemes on the host and check
+    their other arguments as the plain calls do."""
+    k = kv()
+    big = 1 << 40
+    dec, sel = lib.santa_decode_attention_ex, lib.santa_select_teams_ex
+    for bad in (3, -1):
+        assert dec(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, bad, FAKE, None, None, None, FAKE, big, None) == SHAPE
+        assert sel(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, bad, None, None, FAKE, big, None) == SHAPE
+    assert dec(ctypes.byref(k), FAKE, FAKE, 0, 0, 0, 1, FAKE, None, None, None, FAKE, big, None) == SHAPE
+    assert dec(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, 2, None, None, None, None, FAKE, big, None) == NULL
+    assert sel(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, 1, None, None, None, big, None) == WS
+    with pytest.raises(ValueError):
+        S.santa_decode_attention_ex(None, None, None, 8, "poisson")
