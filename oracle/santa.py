@@ -52,6 +52,15 @@ Readings taken where the pages leave a step open (each repeated where used):
       min(1, w) (systematic: the points are one unit apart) and
       1 - prod_j (1 - |[a, a + w) n [j, j + 1)|) (stratified: one
       independent point per unit). Full coverage (R6) is unchanged.
+  R11 hash-partitioned teams ([EXP] section 三 step 1 clusters the keys into
+      teams; section 八 pitfall 3 names sequential, hash and cluster
+      partitions and asks for a configurable one). Per (sequence, KV head),
+      token i gets the code whose bit j (most significant first) is
+      [k_i . r_j > 0] for caller-supplied directions r_j, the dot product a
+      float64 sum in channel order of exact products; the tokens are stably
+      sorted by code and cut into runs of T, so team t holds sorted
+      positions tT .. tT + T - 1 (the last team may be short). The cache
+      is rewritten in that order, so every other step is unchanged.
 
 Parity pins (tests/test_oracle_pins.py): dense attention against torch's
 scaled_dot_product_attention; full coverage against dense; brute-force
@@ -174,6 +183,67 @@ def build_reps_kind(k_pages, page_table, seq_lens, page_size, dtype, kind, seed=
                 i = team_medoid_index(keys[g]) if kind == REP_MEDOID else team_random_index(n, seed, b, t, g)
                 reps[b, t, g] = keys[g, i]
     return reps
+
+
+# ----------------------------------------------------------------------------
+# Hash-partitioned teams (reading R11)
+# ----------------------------------------------------------------------------
+
+def hash_codes(keys, directions):
+    """Code of each key [L][d] for directions [bits][d] (R11): bit j, most
+    significant first, is 1 when the channel-ordered float64 dot product with
+    direction j is > 0. The products (of a bfloat16 or float32 key and a
+    float32 direction) are exact in float64."""
+    keys = np.asarray(keys, dtype=np.float64)
+    dirs = np.asarray(directions, dtype=np.float64)
+    L, d = keys.shape
+    code = np.zeros(L, dtype=np.int64)
+    for j in range(dirs.shape[0]):
+        dot = np.zeros(L)
+        for c in range(d):
+            dot = dot + keys[:, c] * dirs[j, c]
+        code = 2 * code + (dot > 0)
+    return code
+
+
+def hash_partition_order(keys, directions):
+    """Token order of the hash partition (R11): a stable sort by code."""
+    return np.argsort(hash_codes(keys, directions), kind="stable")
+
+
+def cluster_pages(k_pages, v_pages, page_table, seq_lens, page_size, dtype, directions):
+    """The cache rewritten in hash-partition order (R11).
+
+    k_pages, v_pages: stored pages [num_pages][Hkv][T][d]; directions:
+    float32 [Hkv][bits][d]. Returns (k, v, codes, token_of): the rewritten
+    pages (slots past a sequence's end are zero), the code of every original
+    token and the original token at every new position, both [B][Hkv][P*T]
+    with -1 past the sequence's end. Pages outside the sequences' teams are
+    copied unchanged.
+    """
+    _, hkv, T, d = k_pages.shape
+    B, P = np.asarray(page_table).shape
+    k2, v2 = k_pages.copy(), v_pages.copy()
+    codes = np.full((B, hkv, P * T), -1, dtype=np.int64)
+    token_of = np.full((B, hkv, P * T), -1, dtype=np.int64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        K = num_teams(L, T)
+        pages = np.asarray(page_table[b][:K], dtype=np.int64)
+        for g in range(hkv):
+            keys = k_pages[pages, g].reshape(K * T, d)[:L]
+            vals = v_pages[pages, g].reshape(K * T, d)[:L]
+            c = hash_codes(decode(keys, dtype), directions[g])
+            order = np.argsort(c, kind="stable")
+            codes[b, g, :L] = c
+            token_of[b, g, :L] = order
+            nk = np.zeros((K * T, d), dtype=k_pages.dtype)
+            nv = np.zeros((K * T, d), dtype=v_pages.dtype)
+            nk[:L] = keys[order]
+            nv[:L] = vals[order]
+            k2[pages, g] = nk.reshape(K, T, d)
+            v2[pages, g] = nv.reshape(K, T, d)
+    return k2, v2, codes, token_of
 
 
 # ----------------------------------------------------------------------------

@@ -17,6 +17,7 @@ The workloads stand in for the KV caches of the model the SANTA++ abstract
 evaluates (Qwen2.5-7B-Instruct at 32K context: 28 query heads over 4 KV
 heads, head dimension 128); no model weights or evaluation data are used.
 """
+import dataclasses
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
@@ -283,6 +284,16 @@ def paged_ragged(data_seed=5, num_seqs=16, len_min=4096, len_max=65536, T=128, M
 
 
 # The five workloads at their full sizes, by name.
+def hash_directions(data_seed=7, hkv=4, bits=8, d=128):
+    """Directions of a hash partition: float32 N(0, 1), [Hkv][bits][d]."""
+    return np.random.default_rng(data_seed).standard_normal((hkv, bits, d), dtype=np.float32)
+
+
+def permuted_workload(w, k_pages, v_pages, suffix="hashed"):
+    """A copy of workload w whose pages are replaced (same page table and lengths)."""
+    return dataclasses.replace(w, name=f"{w.name}_{suffix}", k_pages=k_pages, v_pages=v_pages)
+
+
 FULL_SIZE = {
     "tiny_f32_n1024_m8": lambda: tiny_planted(),
     "qwen7b_32k_b1_m31": lambda: qwen_planted(),

@@ -561,3 +561,100 @@ def test_variance_reduced_schemes_lower_the_error():
     for scheme in (santa.DRAW_SYSTEMATIC, santa.DRAW_STRATIFIED):
         assert sd[scheme] < 0.6 * sd[santa.DRAW_IID]
         assert mse[scheme] < 0.75 * mse[santa.DRAW_IID]
+
+
+# --------------------------------------------------------------------------
+# Hash-partitioned teams (reading R11)
+# --------------------------------------------------------------------------
+
+def test_hash_code_bits_follow_the_direction_order():
+    # Directions = the first basis vectors: bit j (most significant first) is
+    # the sign of channel j.
+    rng = np.random.default_rng(50)
+    bits, d = 5, 16
+    dirs = np.eye(d)[:bits]
+    keys = rng.standard_normal((200, d))
+    expect = np.zeros(200, dtype=np.int64)
+    for j in range(bits):
+        expect += (keys[:, j] > 0).astype(np.int64) << (bits - 1 - j)
+    assert np.array_equal(santa.hash_codes(keys, dirs), expect)
+    assert np.array_equal(santa.hash_codes(-keys, dirs), (2 ** bits - 1) - expect)   # no exact zeros here
+
+
+def test_hash_codes_match_exact_rational_signs():
+    rng = np.random.default_rng(51)
+    keys = numerics.round_to_dtype(rng.standard_normal((60, 24)), "bf16")
+    dirs = rng.standard_normal((6, 24)).astype(np.float32).astype(np.float64)
+    codes = santa.hash_codes(keys, dirs)
+    for i in range(60):
+        c = 0
+        for j in range(6):
+            exact = sum(Fraction(float(a)) * Fraction(float(r)) for a, r in zip(keys[i], dirs[j]))
+            c = 2 * c + (1 if exact > 0 else 0)
+        assert codes[i] == c
+
+
+def test_hash_order_is_a_stable_sort_that_groups_clusters():
+    rng = np.random.default_rng(54)
+    d, bits = 32, 6
+    dirs = rng.standard_normal((bits, d))
+    centres = rng.standard_normal((4, d)) * 4.0
+    label = rng.integers(0, 4, 400)
+    keys = centres[label] + 0.05 * rng.standard_normal((400, d))
+    order = santa.hash_partition_order(keys, dirs)
+    codes = santa.hash_codes(keys, dirs)
+    assert sorted(order.tolist()) == list(range(400))
+    assert np.all(np.diff(codes[order]) >= 0)
+    for c in set(codes.tolist()):                       # equal codes keep token order
+        pos = order[codes[order] == c]
+        assert np.all(np.diff(pos) > 0)
+    # With these inputs every cluster has one code of its own (no direction
+    # cuts a cluster), so each cluster is one run of the order.
+    per = [set(codes[label == c].tolist()) for c in range(4)]
+    assert all(len(x) == 1 for x in per) and len(set.union(*per)) == 4
+    assert 1 + np.count_nonzero(np.diff(label[order])) == 4
+
+
+def test_cluster_pages_is_a_per_head_permutation_that_keeps_dense_attention():
+    w = wl.paged_ragged(num_seqs=3, len_min=200, len_max=900, T=32, M=8, hq=4, hkv=2, d=32, dtype="bf16")
+    dirs = wl.hash_directions(hkv=2, bits=5, d=32)
+    k2, v2, codes, tok = santa.cluster_pages(w.k_pages, w.v_pages, w.page_table, w.seq_lens, w.page_size,
+                                             w.dtype, dirs)
+    kv0, kv1 = _kv(w), santa.PagedKV(w.dtype, k2, v2, w.page_table, w.seq_lens)
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        for g in range(2):
+            k0, v0 = kv0.all_tokens(b, g)
+            k1, v1 = kv1.all_tokens(b, g)
+            order = tok[b, g, :L]
+            assert np.array_equal(k1, k0[order]) and np.array_equal(v1, v0[order])
+            assert np.all(tok[b, g, L:] == -1) and np.all(codes[b, g, L:] == -1)
+            assert np.array_equal(codes[b, g, :L], santa.hash_codes(k0, dirs[g]))
+        for h in range(4):
+            qh = numerics.decode(w.q[b, h], w.dtype)
+            o0, l0 = santa.dense_head(kv0, qh, b, h, 4)
+            o1, l1 = santa.dense_head(kv1, qh, b, h, 4)
+            assert np.max(np.abs(o0 - o1)) < 1e-12 and abs(l0 - l1) < 1e-12
+
+
+def test_hash_teams_lower_the_error_on_planted_tokens():
+    # A few keys aligned with each query hide among random keys: contiguous
+    # teams dilute them, hash teams gather them, so their representatives
+    # carry the signal and the estimate is far closer to dense attention.
+    w = wl.qwen_planted(batch=1, seq_len=4096, T=32, M=16, hq=4, hkv=1, d=64, plants=8)
+    dirs = wl.hash_directions(hkv=1, bits=7, d=64)
+    k2, v2, _, _ = santa.cluster_pages(w.k_pages, w.v_pages, w.page_table, w.seq_lens, w.page_size, w.dtype,
+                                       dirs)
+    mse = {}
+    for name, ww in (("contiguous", w), ("hashed", wl.permuted_workload(w, k2, v2))):
+        kv = _kv(ww)
+        reps = santa.build_reps(ww.k_pages, ww.page_table, ww.seq_lens, ww.page_size, ww.dtype)
+        err = []
+        for h in range(4):
+            qh = numerics.decode(ww.q[0, h], ww.dtype)
+            out_d, _ = santa.dense_attention(qh, *kv.all_tokens(0, 0))
+            for seed in range(60):
+                r = santa.santa_head(kv, qh, reps, 0, h, 4, ww.M, seed, 0)
+                err.append(np.sum((r.out - out_d) ** 2))
+        mse[name] = np.mean(err)
+    assert mse["hashed"] < 0.5 * mse["contiguous"]
