@@ -270,6 +270,51 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False):
                               "kv_read_fraction": {"per_query_head": round(abs_["frac_head"], 4),
                                                    "hbm": round(abs_["frac_hbm"], 4)}}
 
+    # Hash-partitioned teams: the pack that writes them (from plain pages),
+    # SANTA++ on them, their bytes, and the estimate's error against dense
+    # attention for contiguous and hashed teams (mean over heads of
+    # ||out - dense|| / ||dense||, over 16 draw offsets).
+    from sampled_sparse_decode_amd import workloads as W
+    K = max(1, -(-int(w.seq_lens.max()) // w.page_size))
+    bits = min(10, max(1, math.ceil(math.log2(K))))
+    dirs = torch.from_numpy(W.hash_directions(hkv=w.num_kv_heads, bits=bits, d=w.head_dim)).to(dev)
+    k_src = S.storage_tensor(w.k_pages, w.dtype, dev)
+    v_src = S.storage_tensor(w.v_pages, w.dtype, dev)
+    hcache = [S.KVCache(torch.empty_like(kv.k_pages), torch.empty_like(kv.v_pages), kv.page_table, kv.seq_lens,
+                        w.num_q_heads, w.page_size) for kv in cache]
+    codes = torch.empty((w.batch, w.num_kv_heads, w.max_pages_per_seq * w.page_size), dtype=torch.int32,
+                        device=dev)
+    token_of = torch.empty_like(codes)
+
+    def hpack_step(i):
+        S.santa_pack_pages_hashed(hcache[i % R], k_src, v_src, dirs, codes, token_of)
+
+    hp_us, _ = median_graph(hpack_step, R, max(R, steps // 4), max(R, warmup // 4), torch)
+    for j in range(R):
+        hpack_step(j)
+    del k_src, v_src
+    hreps = [S.santa_build_reps(kv) for kv in hcache]
+    _, _, smp, _ = S.santa_decode_attention(hcache[0], q, hreps[0], M, w.seed, w.offset, wss[0], return_sets=True)
+    torch.cuda.synchronize()
+    abh = algorithmic_bytes(w, union_stats(w, smp.cpu().numpy()))
+
+    def hsanta_step(i):
+        j = i % R
+        S.santa_decode_attention(hcache[j], q, hreps[j], M, w.seed, w.offset, wss[j], out, lse)
+
+    hs_us, _ = median_graph(hsanta_step, R, steps, warmup, torch)
+    dense_out, _ = S.dense_decode_attention(kv0, q, wss[0])
+    errs = {"contiguous": [], "hashed": []}
+    for off in range(16):
+        for name, kv, rp in (("contiguous", kv0, reps[0]), ("hashed", hcache[0], hreps[0])):
+            o, _ = S.santa_decode_attention(kv, q, rp, M, w.seed, w.offset + 1000 + off, wss[0])
+            errs[name].append(((o - dense_out).norm(dim=-1) / dense_out.norm(dim=-1)).mean().item())
+    r["hashed"] = {"bits": bits, "pack_us": round(hp_us, 2), "santa_us_per_layer": round(hs_us, 3),
+                   "kv_read_fraction": {"per_query_head": round(abh["frac_head"], 4),
+                                        "hbm": round(abh["frac_hbm"], 4)},
+                   "estimate_rel_error": {k: round(float(np.mean(v)), 4) for k, v in errs.items()}}
+    del hcache, hreps
+
     # Representative upkeep of one decode step: every sequence's last token is
     # taken as just appended (lengths one less before), its team refreshed.
     prev = (kv0.seq_lens - 1).clamp(min=0)
@@ -351,6 +396,7 @@ def main():
         "update_reps_us": round(r["update_reps_us"], 3),
         "build_reps_us": {k: round(v, 2) for k, v in r["build_reps_us"].items()},
         "draw_schemes": r["schemes"],
+        "hashed_teams": r["hashed"],
         "roofline": {"kernel": "gather+combine (santa_attend_selected)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
@@ -370,7 +416,8 @@ def main():
                        "dense_frac_of_peak": round(gbps(a["dense"], rs["dense_us"]) / HBM_PEAK_GBPS, 4),
                        "kv_read_fraction_hbm": round(a["frac_hbm"], 4),
                        "build_reps_us": {k: round(v, 2) for k, v in rs["build_reps_us"].items()},
-                       "draw_schemes": rs["schemes"]}
+                       "draw_schemes": rs["schemes"],
+                       "hashed_teams": rs["hashed"]}
         del ws
         torch.cuda.empty_cache()
     if scale:

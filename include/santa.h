@@ -289,6 +289,35 @@ santa_status santa_pack_pages(int32_t dtype, int64_t num_pages, int32_t num_kv_h
                               const void *k_src, const void *v_src, void *k_dst, void *v_dst,
                               void *stream);
 
+/* Hash-partitioned teams ([EXP] section 三 step 1: keys are clustered into
+ * teams; section 八 pitfall 3: the partition may be sequential, hash or
+ * cluster). Writes the cache pages of every sequence with its tokens, per KV
+ * head, in the order of a sign-hash partition, so that team t (page
+ * page_table[b][t]) holds tokens of similar direction; all other entry
+ * points then run on these teams unchanged. For sequence b and KV head g,
+ * token i (i < L_b) gets code_i whose bit j, most significant first, is
+ * [k_i . r_gj > 0], the dot product a float64 sum in channel order; the
+ * tokens are stably sorted by code (equal codes keep token order) and the
+ * token at sorted position s is written to team s / T, slot s % T. Slots
+ * past L_b in the last team are zero.
+ *   kv          destination cache: k_pages / v_pages are written (tile order,
+ *               see "Paged KV layout"); page_table, seq_lens as usual. A
+ *               page may belong to one sequence only. Pages outside the
+ *               sequences' first K_b table entries are not written.
+ *   k_src, v_src  the same pages in plain [num_pages][Hkv][T][d] order
+ *               (distinct from the destination: SANTA_ERR_SHAPE otherwise)
+ *   directions  [Hkv][bits][d] float32, device
+ *   bits        1 .. 10
+ *   codes       [B][Hkv][max_pages_per_seq * T] int32 out: code of token i,
+ *               -1 for i >= L_b
+ *   token_of    [B][Hkv][max_pages_per_seq * T] int32 out: the token at
+ *               sorted position s, -1 for s >= L_b
+ * Tokens appended later go to the end in arrival order (santa_update_reps
+ * keeps their team's representative); packing again re-partitions. */
+santa_status santa_pack_pages_hashed(const santa_kv *kv, const void *k_src, const void *v_src,
+                                     const float *directions, int32_t bits,
+                                     int32_t *codes, int32_t *token_of, void *stream);
+
 /* Static description of a status code. */
 const char *santa_status_string(int32_t status);
 

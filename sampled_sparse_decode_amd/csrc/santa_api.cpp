@@ -329,6 +329,43 @@ santa_status santa_pack_pages(int32_t dtype, int64_t num_pages, int32_t num_kv_h
     return launch_pack_pages(pp, stream);
 }
 
+santa_status santa_pack_pages_hashed(const santa_kv *kv, const void *k_src, const void *v_src,
+                                     const float *directions, int32_t bits,
+                                     int32_t *codes, int32_t *token_of, void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!k_src || !v_src || !directions || !codes || !token_of) return SANTA_ERR_NULL;
+    if (bits < 1 || bits > kMaxHashBits) return SANTA_ERR_SHAPE;
+    const int64_t positions = int64_t(kv->batch) * kv->num_kv_heads * kv->max_pages_per_seq * kv->page_size;
+    if (positions >= (int64_t(1) << 31)) return SANTA_ERR_SHAPE;
+    // Source and destination pages must be distinct buffers.
+    const uintptr_t bytes = uintptr_t(kv->num_pages) * uintptr_t(kv->num_kv_heads) * uintptr_t(kv->page_size) *
+                            uintptr_t(kv->head_dim) * (kv->dtype == SANTA_BF16 ? 2u : 4u);
+    const uintptr_t lo[4] = {uintptr_t(k_src), uintptr_t(v_src), uintptr_t(kv->k_pages), uintptr_t(kv->v_pages)};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if ((i >= 2 || j >= 2) && lo[i] < lo[j] + bytes && lo[j] < lo[i] + bytes) return SANTA_ERR_SHAPE;
+    ClusterParams c{};
+    c.k_src = k_src;
+    c.v_src = v_src;
+    c.k_dst = const_cast<void *>(kv->k_pages);
+    c.v_dst = const_cast<void *>(kv->v_pages);
+    c.directions = directions;
+    c.page_table = kv->page_table;
+    c.seq_lens = kv->seq_lens;
+    c.codes = codes;
+    c.token_of = token_of;
+    c.num_pages = kv->num_pages;
+    c.dtype = kv->dtype;
+    c.B = kv->batch;
+    c.Hkv = kv->num_kv_heads;
+    c.P = kv->max_pages_per_seq;
+    c.T = kv->page_size;
+    c.d = kv->head_dim;
+    c.bits = bits;
+    return launch_pack_hashed(c, stream);
+}
+
 const char *santa_status_string(int32_t status) {
     switch (status) {
         case SANTA_OK: return "ok";
@@ -341,6 +378,6 @@ const char *santa_status_string(int32_t status) {
     }
 }
 
-int32_t santa_version(void) { return 220; }
+int32_t santa_version(void) { return 230; }
 
 }  // extern "C"

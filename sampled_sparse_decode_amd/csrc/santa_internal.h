@@ -77,6 +77,22 @@ struct PackParams {
     int32_t dtype, T, d;
 };
 
+// santa_pack_pages_hashed arguments.
+constexpr int kMaxHashBits = 10;
+struct ClusterParams {
+    const void *k_src;          // plain pages [num_pages][Hkv][T][d]
+    const void *v_src;
+    void *k_dst;                // tile-order pages [num_pages][Hkv][T * d]
+    void *v_dst;
+    const float *directions;    // [Hkv][bits][d]
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    int32_t *codes;             // [B][Hkv][P * T]
+    int32_t *token_of;          // [B][Hkv][P * T]
+    int64_t num_pages;
+    int32_t dtype, B, Hkv, P, T, d, bits;
+};
+
 // Host-side argument checks; no HIP calls.
 santa_status validate_kv(const santa_kv *kv);
 
@@ -87,5 +103,6 @@ santa_status launch_given(const Params &p, void *stream);
 santa_status launch_gather(const Params &p, void *stream);
 santa_status launch_combine(const Params &p, void *stream);
 santa_status launch_pack_pages(const PackParams &pp, void *stream);
+santa_status launch_pack_hashed(const ClusterParams &c, void *stream);
 
 }  // namespace santa

@@ -31,6 +31,7 @@ EXPORTED = (
     "dense_decode_attention",
     "santa_attention_given_teams",
     "santa_pack_pages",
+    "santa_pack_pages_hashed",
     "santa_status_string",
     "santa_version",
 )
@@ -89,6 +90,7 @@ def load():
         "dense_decode_attention": (i32, [kvp, P, P, P, P, sz, P]),
         "santa_attention_given_teams": (i32, [kvp, P, i32, P, P, P, P, P, sz, P]),
         "santa_pack_pages": (i32, [i32, ctypes.c_int64, i32, i32, i32, P, P, P, P, P]),
+        "santa_pack_pages_hashed": (i32, [kvp, P, P, P, i32, P, P, P]),
         "santa_status_string": (ctypes.c_char_p, [i32]),
         "santa_version": (i32, []),
     }
@@ -170,6 +172,47 @@ def pack_pages(k_src, v_src, k_dst=None, v_dst=None):
     _check("santa_pack_pages", load().santa_pack_pages(_DTYPES[k_src.dtype], n, hkv, T, d, _ptr(k_src), _ptr(v_src),
                                                       _ptr(k_dst), _ptr(v_dst), _stream()))
     return k_dst, v_dst
+
+
+def santa_pack_pages_hashed(kv, k_src, v_src, directions, codes=None, token_of=None):
+    """Write kv's pages from plain pages k_src / v_src [num_pages][Hkv][T][d]
+    in hash-partition order for directions [Hkv][bits][d] (float32).
+    Returns (codes, token_of), each [B][Hkv][P*T] int32."""
+    if k_src.shape != (kv.num_pages, kv.num_kv_heads, kv.page_size, kv.head_dim) or v_src.shape != k_src.shape:
+        raise ValueError("k_src and v_src must be [num_pages][Hkv][T][d]")
+    if k_src.dtype != kv.dtype or v_src.dtype != kv.dtype or not (k_src.is_contiguous() and v_src.is_contiguous()):
+        raise ValueError("k_src and v_src must be contiguous tensors of the cache dtype")
+    if (directions.dtype != torch.float32 or directions.dim() != 3 or not directions.is_contiguous()
+            or directions.shape[0] != kv.num_kv_heads or directions.shape[2] != kv.head_dim):
+        raise ValueError("directions must be a contiguous float32 [Hkv][bits][d] tensor")
+    shape = (kv.batch, kv.num_kv_heads, kv.max_pages_per_seq * kv.page_size)
+    if codes is None:
+        codes = torch.empty(shape, dtype=torch.int32, device=kv.device)
+    if token_of is None:
+        token_of = torch.empty(shape, dtype=torch.int32, device=kv.device)
+    d = kv.desc()
+    _check("santa_pack_pages_hashed",
+           load().santa_pack_pages_hashed(ctypes.byref(d), _ptr(k_src), _ptr(v_src), _ptr(directions),
+                                          int(directions.shape[1]), _ptr(codes), _ptr(token_of), _stream()))
+    return codes, token_of
+
+
+def kv_from_workload_hashed(w, directions, device="cuda"):
+    """Upload a workload and pack its pages in hash-partition order.
+    Returns (KVCache, q tensor, codes, token_of)."""
+    k_src = storage_tensor(w.k_pages, w.dtype, device)
+    v_src = storage_tensor(w.v_pages, w.dtype, device)
+    n, hkv, T, d = (int(x) for x in k_src.shape)
+    kv = KVCache(torch.zeros((n, hkv, T * d), dtype=k_src.dtype, device=device),
+                 torch.zeros((n, hkv, T * d), dtype=k_src.dtype, device=device),
+                 torch.from_numpy(np.ascontiguousarray(w.page_table, dtype=np.int32)).to(device),
+                 torch.from_numpy(np.ascontiguousarray(w.seq_lens, dtype=np.int32)).to(device),
+                 w.num_q_heads, w.page_size)
+    dirs = torch.from_numpy(np.ascontiguousarray(directions, dtype=np.float32)).to(device)
+    codes, token_of = santa_pack_pages_hashed(kv, k_src, v_src, dirs)
+    torch.cuda.current_stream().synchronize()
+    del k_src, v_src
+    return kv, storage_tensor(w.q, w.dtype, device), codes, token_of
 
 
 def storage_tensor(arr, dtype, device):

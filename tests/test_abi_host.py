@@ -46,7 +46,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.santa_version() == 220
+    assert lib.santa_version() == 230
     for code in range(6):
         assert S.santa_status_string(code)
     assert S.santa_status_string(99) == "unknown status"
@@ -187,3 +187,20 @@ def test_draw_scheme_validation(lib):
     assert sel(ctypes.byref(k), FAKE, FAKE, 8, 0, 0, 1, None, None, None, big, None) == WS
     with pytest.raises(ValueError):
         S.santa_decode_attention_ex(None, None, None, 8, "poisson")
+
+
+def test_pack_pages_hashed_validation(lib):
+    """santa_pack_pages_hashed checks its arguments on the host."""
+    k = kv(v_pages=FAKE + (3 << 40))          # distinct destination buffers
+    call = lib.santa_pack_pages_hashed
+    far = ctypes.c_void_p(FAKE + (1 << 40))
+    far2 = ctypes.c_void_p(FAKE + (2 << 40))
+    F = ctypes.c_void_p(FAKE)
+    assert call(ctypes.byref(k), None, far2, F, 4, F, F, None) == NULL
+    assert call(ctypes.byref(k), far, far2, None, 4, F, F, None) == NULL
+    assert call(ctypes.byref(k), far, far2, F, 4, None, F, None) == NULL
+    assert call(ctypes.byref(k), far, far2, F, 0, F, F, None) == SHAPE
+    assert call(ctypes.byref(k), far, far2, F, 11, F, F, None) == SHAPE
+    assert call(ctypes.byref(k), F, far2, F, 4, F, F, None) == SHAPE          # source overlaps destination
+    assert call(ctypes.byref(kv()), far, far2, F, 4, F, F, None) == SHAPE     # destinations overlap
+    assert call(ctypes.byref(kv(head_dim=80)), far, far2, F, 4, F, F, None) == UNSUP
