@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--scale", default="qwen7b_32k_b8_m32,mixture_128k_b4_t256_m64",
                     help="workloads also measured, compactly, after the headline one ('' = none)")
     ap.add_argument("--scale-steps", type=int, default=100)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the decode path (no draw schemes, hashed teams or representative builds)")
     return ap.parse_args()
 
 
@@ -206,7 +208,7 @@ def cpu_baseline(w, budget_s):
                       f"representatives precomputed; scaled to one layer"}
 
 
-def measure(w, steps, warmup, layers, torch, S, calibrate=False):
+def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
     """Times SANTA++, dense and the attend stage on workload w (inputs resident,
     the layer's cache cycled over R copies). Returns a dict of results."""
     dev = torch.device("cuda:0")
@@ -252,68 +254,70 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False):
     torch.cuda.synchronize()
     r["attend_us"], _ = median_graph(attend_step, R, steps, warmup, torch)
 
-    # The variance-reduced draw schemes: whole decode call, and the bytes of
-    # their (larger: fewer repeated teams) unions.
-    r["schemes"] = {}
-    for name in ("systematic", "stratified"):
-        _, _, smp, _ = S.santa_decode_attention_ex(kv0, q, reps[0], M, name, w.seed, w.offset, wss[0],
-                                                   return_sets=True)
+    r["schemes"], r["hashed"] = None, None
+    if extras:
+        # The variance-reduced draw schemes: whole decode call, and the bytes of
+        # their (larger: fewer repeated teams) unions.
+        r["schemes"] = {}
+        for name in ("systematic", "stratified"):
+            _, _, smp, _ = S.santa_decode_attention_ex(kv0, q, reps[0], M, name, w.seed, w.offset, wss[0],
+                                                       return_sets=True)
+            torch.cuda.synchronize()
+            abs_ = algorithmic_bytes(w, union_stats(w, smp.cpu().numpy()))
+
+            def scheme_step(i, name=name):
+                j = i % R
+                S.santa_decode_attention_ex(cache[j], q, reps[j], M, name, w.seed, w.offset, wss[j], out, lse)
+
+            us, _ = median_graph(scheme_step, R, steps, warmup, torch)
+            r["schemes"][name] = {"us_per_layer": round(us, 3),
+                                  "kv_read_fraction": {"per_query_head": round(abs_["frac_head"], 4),
+                                                       "hbm": round(abs_["frac_hbm"], 4)}}
+
+        # Hash-partitioned teams: the pack that writes them (from plain pages),
+        # SANTA++ on them, their bytes, and the estimate's error against dense
+        # attention for contiguous and hashed teams (mean over heads of
+        # ||out - dense|| / ||dense||, over 16 draw offsets).
+        from sampled_sparse_decode_amd import workloads as W
+        K = max(1, -(-int(w.seq_lens.max()) // w.page_size))
+        bits = min(10, max(1, math.ceil(math.log2(K))))
+        dirs = torch.from_numpy(W.hash_directions(hkv=w.num_kv_heads, bits=bits, d=w.head_dim)).to(dev)
+        k_src = S.storage_tensor(w.k_pages, w.dtype, dev)
+        v_src = S.storage_tensor(w.v_pages, w.dtype, dev)
+        hcache = [S.KVCache(torch.empty_like(kv.k_pages), torch.empty_like(kv.v_pages), kv.page_table, kv.seq_lens,
+                            w.num_q_heads, w.page_size) for kv in cache]
+        codes = torch.empty((w.batch, w.num_kv_heads, w.max_pages_per_seq * w.page_size), dtype=torch.int32,
+                            device=dev)
+        token_of = torch.empty_like(codes)
+
+        def hpack_step(i):
+            S.santa_pack_pages_hashed(hcache[i % R], k_src, v_src, dirs, codes, token_of)
+
+        hp_us, _ = median_graph(hpack_step, R, max(R, steps // 4), max(R, warmup // 4), torch)
+        for j in range(R):
+            hpack_step(j)
+        del k_src, v_src
+        hreps = [S.santa_build_reps(kv) for kv in hcache]
+        _, _, smp, _ = S.santa_decode_attention(hcache[0], q, hreps[0], M, w.seed, w.offset, wss[0], return_sets=True)
         torch.cuda.synchronize()
-        abs_ = algorithmic_bytes(w, union_stats(w, smp.cpu().numpy()))
+        abh = algorithmic_bytes(w, union_stats(w, smp.cpu().numpy()))
 
-        def scheme_step(i, name=name):
+        def hsanta_step(i):
             j = i % R
-            S.santa_decode_attention_ex(cache[j], q, reps[j], M, name, w.seed, w.offset, wss[j], out, lse)
+            S.santa_decode_attention(hcache[j], q, hreps[j], M, w.seed, w.offset, wss[j], out, lse)
 
-        us, _ = median_graph(scheme_step, R, steps, warmup, torch)
-        r["schemes"][name] = {"us_per_layer": round(us, 3),
-                              "kv_read_fraction": {"per_query_head": round(abs_["frac_head"], 4),
-                                                   "hbm": round(abs_["frac_hbm"], 4)}}
-
-    # Hash-partitioned teams: the pack that writes them (from plain pages),
-    # SANTA++ on them, their bytes, and the estimate's error against dense
-    # attention for contiguous and hashed teams (mean over heads of
-    # ||out - dense|| / ||dense||, over 16 draw offsets).
-    from sampled_sparse_decode_amd import workloads as W
-    K = max(1, -(-int(w.seq_lens.max()) // w.page_size))
-    bits = min(10, max(1, math.ceil(math.log2(K))))
-    dirs = torch.from_numpy(W.hash_directions(hkv=w.num_kv_heads, bits=bits, d=w.head_dim)).to(dev)
-    k_src = S.storage_tensor(w.k_pages, w.dtype, dev)
-    v_src = S.storage_tensor(w.v_pages, w.dtype, dev)
-    hcache = [S.KVCache(torch.empty_like(kv.k_pages), torch.empty_like(kv.v_pages), kv.page_table, kv.seq_lens,
-                        w.num_q_heads, w.page_size) for kv in cache]
-    codes = torch.empty((w.batch, w.num_kv_heads, w.max_pages_per_seq * w.page_size), dtype=torch.int32,
-                        device=dev)
-    token_of = torch.empty_like(codes)
-
-    def hpack_step(i):
-        S.santa_pack_pages_hashed(hcache[i % R], k_src, v_src, dirs, codes, token_of)
-
-    hp_us, _ = median_graph(hpack_step, R, max(R, steps // 4), max(R, warmup // 4), torch)
-    for j in range(R):
-        hpack_step(j)
-    del k_src, v_src
-    hreps = [S.santa_build_reps(kv) for kv in hcache]
-    _, _, smp, _ = S.santa_decode_attention(hcache[0], q, hreps[0], M, w.seed, w.offset, wss[0], return_sets=True)
-    torch.cuda.synchronize()
-    abh = algorithmic_bytes(w, union_stats(w, smp.cpu().numpy()))
-
-    def hsanta_step(i):
-        j = i % R
-        S.santa_decode_attention(hcache[j], q, hreps[j], M, w.seed, w.offset, wss[j], out, lse)
-
-    hs_us, _ = median_graph(hsanta_step, R, steps, warmup, torch)
-    dense_out, _ = S.dense_decode_attention(kv0, q, wss[0])
-    errs = {"contiguous": [], "hashed": []}
-    for off in range(16):
-        for name, kv, rp in (("contiguous", kv0, reps[0]), ("hashed", hcache[0], hreps[0])):
-            o, _ = S.santa_decode_attention(kv, q, rp, M, w.seed, w.offset + 1000 + off, wss[0])
-            errs[name].append(((o - dense_out).norm(dim=-1) / dense_out.norm(dim=-1)).mean().item())
-    r["hashed"] = {"bits": bits, "pack_us": round(hp_us, 2), "santa_us_per_layer": round(hs_us, 3),
-                   "kv_read_fraction": {"per_query_head": round(abh["frac_head"], 4),
-                                        "hbm": round(abh["frac_hbm"], 4)},
-                   "estimate_rel_error": {k: round(float(np.mean(v)), 4) for k, v in errs.items()}}
-    del hcache, hreps
+        hs_us, _ = median_graph(hsanta_step, R, steps, warmup, torch)
+        dense_out, _ = S.dense_decode_attention(kv0, q, wss[0])
+        errs = {"contiguous": [], "hashed": []}
+        for off in range(16):
+            for name, kv, rp in (("contiguous", kv0, reps[0]), ("hashed", hcache[0], hreps[0])):
+                o, _ = S.santa_decode_attention(kv, q, rp, M, w.seed, w.offset + 1000 + off, wss[0])
+                errs[name].append(((o - dense_out).norm(dim=-1) / dense_out.norm(dim=-1)).mean().item())
+        r["hashed"] = {"bits": bits, "pack_us": round(hp_us, 2), "santa_us_per_layer": round(hs_us, 3),
+                       "kv_read_fraction": {"per_query_head": round(abh["frac_head"], 4),
+                                            "hbm": round(abh["frac_hbm"], 4)},
+                       "estimate_rel_error": {k: round(float(np.mean(v)), 4) for k, v in errs.items()}}
+        del hcache, hreps
 
     # Representative upkeep of one decode step: every sequence's last token is
     # taken as just appended (lengths one less before), its team refreshed.
@@ -329,7 +333,7 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False):
     # cost after prefill), into a scratch buffer so the decode reps stay.
     scratch = torch.empty_like(reps[0])
     r["build_reps_us"] = {}
-    for kind in ("mean", "medoid", "random"):
+    for kind in (("mean", "medoid", "random") if extras else ()):
         def build_step(i, kind=kind):
             S.santa_build_reps_ex(cache[i % R], kind, reps=scratch, seed=1)
 
@@ -361,7 +365,7 @@ def main():
 
     torch.cuda.set_device(torch.device("cuda:0"))
     w = W.FULL_SIZE[args.workload]()
-    r = measure(w, args.steps, args.warmup, args.layers, torch, S, args.calibrate)
+    r = measure(w, args.steps, args.warmup, args.layers, torch, S, args.calibrate, not args.no_extras)
     ab = r["ab"]
     santa_us, dense_us, attend_us = r["santa_us"], r["dense_us"], r["attend_us"]
     attend_gbps = gbps(ab["attend"], attend_us)
@@ -407,7 +411,7 @@ def main():
     scale = {}
     for name in [x for x in args.scale.split(",") if x and x != args.workload]:
         ws = W.FULL_SIZE[name]()
-        rs = measure(ws, args.scale_steps, max(10, args.scale_steps // 10), 0, torch, S)
+        rs = measure(ws, args.scale_steps, max(10, args.scale_steps // 10), 0, torch, S, extras=not args.no_extras)
         a = rs["ab"]
         scale[name] = {"santa_us": round(rs["santa_us"], 2), "dense_us": round(rs["dense_us"], 2),
                        "speedup_vs_dense": round(rs["dense_us"] / rs["santa_us"], 3),

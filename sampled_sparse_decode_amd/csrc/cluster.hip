@@ -34,7 +34,7 @@ __device__ __forceinline__ const KV *src_row(const ClusterParams &c, const KV *b
 template <typename KV, int D>
 __global__ __launch_bounds__(kBlock) void hash_codes_kernel(ClusterParams c) {
     constexpr int VPC = KVTraits<KV>::kPerChunk;
-    __shared__ double dir_s[kMaxHashBits][D];
+    __shared__ __attribute__((aligned(16))) double dir_s[kMaxHashBits][D];
     const int g = blockIdx.y, b = blockIdx.z;
     for (int e = threadIdx.x; e < c.bits * D; e += kBlock)
         dir_s[e / D][e % D] = double(c.directions[(size_t(g) * c.bits + e / D) * D + e % D]);
@@ -48,18 +48,26 @@ __global__ __launch_bounds__(kBlock) void hash_codes_kernel(ClusterParams c) {
         return;
     }
     const KV *row = src_row(c, static_cast<const KV *>(c.k_src), b, g, i);
+    uint4 raw[D / VPC];                            // the whole row in one round trip
+#pragma unroll
+    for (int q = 0; q < D / VPC; ++q) raw[q] = ld16(row + q * VPC);
     double dot[kMaxHashBits];
 #pragma unroll
     for (int j = 0; j < kMaxHashBits; ++j) dot[j] = 0.0;
-    for (int ch = 0; ch < D; ch += VPC) {
+#pragma unroll
+    for (int q = 0; q < D / VPC; ++q) {
         float f[8];
-        unpack(ld16(row + ch), f, KV{});
+        unpack(raw[q], f, KV{});
 #pragma unroll
-        for (int e = 0; e < VPC; ++e) {
-            const double k = double(f[e]);
+        for (int j = 0; j < kMaxHashBits; ++j) {
+            if (j < c.bits) {
 #pragma unroll
-            for (int j = 0; j < kMaxHashBits; ++j)
-                if (j < c.bits) dot[j] = fma(k, dir_s[j][ch + e], dot[j]);   // product exact: fma = add
+                for (int e = 0; e < VPC; e += 2) {       // channel order; products exact: fma = add
+                    const double2 r = *reinterpret_cast<const double2 *>(&dir_s[j][q * VPC + e]);
+                    dot[j] = fma(double(f[e]), r.x, dot[j]);
+                    dot[j] = fma(double(f[e + 1]), r.y, dot[j]);
+                }
+            }
         }
     }
     int code = 0;
@@ -95,7 +103,20 @@ __global__ __launch_bounds__(kSortThreads) void hash_rank_kernel(ClusterParams c
     __syncthreads();
     const int per = (L + kSortWaves - 1) / kSortWaves;
     const int lo = min(L, wave * per), hi = min(L, lo + per);
-    for (int i = lo + lane; i < hi; i += 64) atomicAdd(&hist[wave][codes[i] & (nb - 1)], 1);
+    // Codes are loaded kBatch groups of 64 at a time, so a pass waits for
+    // memory once per batch rather than once per group.
+    constexpr int kBatch = 16;
+    for (int i0 = lo; i0 < hi; i0 += 64 * kBatch) {
+        int cb[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = i0 + 64 * u + lane;
+            cb[u] = i < hi ? codes[i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (cb[u] >= 0) atomicAdd(&hist[wave][cb[u] & (nb - 1)], 1);
+    }
     __syncthreads();
 
     // Exclusive scan of the code totals (thread = code), then the cursors.
@@ -121,32 +142,46 @@ __global__ __launch_bounds__(kSortThreads) void hash_rank_kernel(ClusterParams c
     __syncthreads();
 
     const uint64_t below = (uint64_t(1) << lane) - 1;
-    for (int i0 = lo; i0 < hi; i0 += 64) {
-        const int i = i0 + lane;
-        const bool valid = i < hi;
-        const int code = valid ? (codes[i] & (nb - 1)) : 0;
-        uint64_t same = __ballot(valid);
-        for (int j = 0; j < c.bits; ++j) {
-            const bool bit = (code >> j) & 1;
-            const uint64_t ones = __ballot(valid && bit);
-            same &= bit ? ones : ~ones;
+    for (int b0 = lo; b0 < hi; b0 += 64 * kBatch) {
+        int cb[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = b0 + 64 * u + lane;
+            cb[u] = i < hi ? codes[i] : -1;
         }
-        const int rank = __popcll(same & below);
-        const int cursor = valid ? hist[wave][code] : 0;
-        if (valid && cursor + rank < cap) token_of[cursor + rank] = i;
-        __builtin_amdgcn_wave_barrier();
-        if (valid && rank == 0) hist[wave][code] = cursor + __popcll(same);   // the group's first lane
-        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = b0 + 64 * u + lane;
+            const bool valid = i < hi;
+            const int code = valid ? (cb[u] & (nb - 1)) : 0;
+            uint64_t same = __ballot(valid);
+            for (int j = 0; j < c.bits; ++j) {
+                const bool bit = (code >> j) & 1;
+                const uint64_t ones = __ballot(valid && bit);
+                same &= bit ? ones : ~ones;
+            }
+            const int rank = __popcll(same & below);
+            const int cursor = valid ? hist[wave][code] : 0;
+            if (valid && cursor + rank < cap) token_of[cursor + rank] = i;
+            __builtin_amdgcn_wave_barrier();
+            if (valid && rank == 0) hist[wave][code] = cursor + __popcll(same);   // the group's first lane
+            __builtin_amdgcn_wave_barrier();
+        }
     }
 }
 
 // 3. Team tile t of (sequence b, KV head g) from the plain source rows of
 //    the tokens at sorted positions tT .. tT + T - 1 (zeros past the end),
-//    written in the cache's tile order.
-template <typename KV>
+//    written in the cache's tile order, one chunk of C tokens at a time.
+//    Key pieces are 16-byte runs of one source row, copied directly; the
+//    chunk's value rows are first staged in LDS with whole-row loads (rows
+//    padded by one 4-byte bank), then written channel-major.
+template <typename KV, int D>
 __global__ __launch_bounds__(kBlock) void pack_hashed_kernel(ClusterParams c) {
     constexpr int VPC = KVTraits<KV>::kPerChunk;
+    constexpr int RP = D + 4 / int(sizeof(KV));          // padded LDS row
     __shared__ int32_t src_s[256];
+    __shared__ __attribute__((aligned(16))) KV v_s[32][RP];
     const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int cap = c.P * c.T;
     const int L = clamp_len(c.seq_lens[b], cap);
@@ -158,33 +193,36 @@ __global__ __launch_bounds__(kBlock) void pack_hashed_kernel(ClusterParams c) {
     }
     __syncthreads();
     const int64_t page = clamp_page(c.page_table[size_t(b) * c.P + t], c.num_pages);
-    const size_t tile = (size_t(page) * c.Hkv + g) * size_t(c.T) * c.d;
+    const size_t tile = (size_t(page) * c.Hkv + g) * size_t(c.T) * D;
     KV *kd = static_cast<KV *>(c.k_dst) + tile;
     KV *vd = static_cast<KV *>(c.v_dst) + tile;
     const KV *ks = static_cast<const KV *>(c.k_src);
     const KV *vs = static_cast<const KV *>(c.v_src);
     const int C = chunk_tokens(c.T);
-    const int pieces = c.T * c.d / VPC;
-    for (int j = threadIdx.x; j < pieces; j += kBlock) {
-        const int e = j * VPC;
-        const int chunk = e / (C * c.d), r = e - chunk * (C * c.d);
-        {   // keys: VPC consecutive channels of one token
-            const int slab = r / (C * 32), r2 = r - slab * (C * 32);
-            const int s = chunk * C + r2 / 32, ch = slab * 32 + (r2 & 31);
-            const int i = src_s[s];
-            *reinterpret_cast<uint4 *>(kd + e) =
-                i >= 0 ? ld16(src_row(c, ks, b, g, i) + ch) : make_uint4(0, 0, 0, 0);
+    constexpr int RPC = D / VPC;                          // 16-byte pieces per row
+    for (int chunk = 0; chunk < c.T / C; ++chunk) {
+        KV *kc = kd + size_t(chunk) * C * D;
+        KV *vc = vd + size_t(chunk) * C * D;
+        for (int q = threadIdx.x; q < C * RPC; q += kBlock) {
+            const int s = q / RPC, col = (q % RPC) * VPC;
+            const int i = src_s[chunk * C + s];
+            const uint4 kx = i >= 0 ? ld16(src_row(c, ks, b, g, i) + col) : make_uint4(0, 0, 0, 0);
+            const uint4 vx = i >= 0 ? ld16(src_row(c, vs, b, g, i) + col) : make_uint4(0, 0, 0, 0);
+            // keys: slab col / 32, token s, channels col % 32 ..
+            *reinterpret_cast<uint4 *>(kc + (col >> 5) * (C * 32) + s * 32 + (col & 31)) = kx;
+            const KV *vxe = reinterpret_cast<const KV *>(&vx);
+#pragma unroll
+            for (int u = 0; u < VPC; ++u) v_s[s][col + u] = vxe[u];
         }
-        {   // values: VPC consecutive tokens of one channel
-            const int ch = r / C, s0 = chunk * C + (r - ch * C);
+        __syncthreads();
+        for (int q = threadIdx.x; q < C * RPC; q += kBlock) {
+            const int ch = q / (C / VPC), s0 = (q % (C / VPC)) * VPC;
             KV x[VPC];
 #pragma unroll
-            for (int u = 0; u < VPC; ++u) {
-                const int i = src_s[s0 + u];
-                x[u] = i >= 0 ? src_row(c, vs, b, g, i)[ch] : KV(0);
-            }
-            *reinterpret_cast<uint4 *>(vd + e) = *reinterpret_cast<const uint4 *>(x);
+            for (int u = 0; u < VPC; ++u) x[u] = v_s[s0 + u][ch];
+            *reinterpret_cast<uint4 *>(vc + ch * C + s0) = *reinterpret_cast<const uint4 *>(x);
         }
+        __syncthreads();
     }
 }
 
@@ -206,8 +244,13 @@ santa_status launch_pack_hashed(const ClusterParams &c, void *stream) {
     s = launched();
     if (s != SANTA_OK) return s;
     const dim3 pgrid(c.P, c.Hkv, c.B);
-    if (c.dtype == SANTA_BF16) hipLaunchKernelGGL((pack_hashed_kernel<bf16_t>), pgrid, dim3(kBlock), 0, st, c);
-    else hipLaunchKernelGGL((pack_hashed_kernel<float>), pgrid, dim3(kBlock), 0, st, c);
+    if (c.dtype == SANTA_BF16) {
+        if (c.d == 64) hipLaunchKernelGGL((pack_hashed_kernel<bf16_t, 64>), pgrid, dim3(kBlock), 0, st, c);
+        else hipLaunchKernelGGL((pack_hashed_kernel<bf16_t, 128>), pgrid, dim3(kBlock), 0, st, c);
+    } else {
+        if (c.d == 64) hipLaunchKernelGGL((pack_hashed_kernel<float, 64>), pgrid, dim3(kBlock), 0, st, c);
+        else hipLaunchKernelGGL((pack_hashed_kernel<float, 128>), pgrid, dim3(kBlock), 0, st, c);
+    }
     return launched();
 }
 
