@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import numerics
 from oracle import santa as O
 from sampled_sparse_decode_amd import santa as S
 from sampled_sparse_decode_amd import workloads as W
@@ -102,3 +103,47 @@ def test_systematic_draws_m_distinct_teams_on_flat_scores():
     teams = teams.cpu().numpy()
     assert np.all(teams >= 0)                                   # M distinct teams in every head
     assert np.allclose(inv_pi.cpu().numpy(), K / M, rtol=1e-6)
+
+
+FULL = {
+    "qwen7b_32k_b1_m31": [(0, 0), (0, 13), (0, 27)],
+    "qwen7b_32k_b8_m32": [(0, 1), (7, 27)],
+    "mixture_128k_b4_t256_m64": [(2, 11)],
+}
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("name", list(FULL))
+def test_scheme_full_size_sampled_heads(name, scheme):
+    # Full-size configurations in the launch configuration the benchmark
+    # times; the oracle evaluates a sample of heads one by one.
+    w = W.FULL_SIZE[name]()
+    pairs = FULL[name]
+    print(f"[scheme full] {scheme} {name} B={w.batch} P={w.num_pages} heads={pairs}", flush=True)
+    kv, q = S.kv_from_workload(w)
+    reps = S.santa_build_reps(kv)
+    out, lse, teams, inv_pi = S.santa_decode_attention_ex(kv, q, reps, w.M, scheme, seed=w.seed, offset=w.offset,
+                                                          return_sets=True)
+    torch.cuda.synchronize()
+    out, lse, teams, inv_pi = (x.cpu().numpy() for x in (out, lse, teams, inv_pi))
+    ref_reps = parity.check_reps(w, reps, pairs)
+    okv = parity.oracle_kv(w)
+    for b, h in pairs:
+        parity.check_santa_head(w, okv, ref_reps, b, h, out[b, h], lse[b, h], teams[b, h], inv_pi[b, h],
+                                scheme=SCHEMES[scheme])
+        if scheme == "systematic":       # every team with M p >= 1 holds a point
+            K = O.num_teams(int(w.seq_lens[b]), w.page_size)
+            g = h // w.group
+            qh = numerics.decode(w.q[b, h], w.dtype)
+            sel = O.select_teams(qh, np.stack([ref_reps[b, t, g] for t in range(K)]), w.M, w.seed, w.offset, b, h,
+                                 O.DRAW_SYSTEMATIC)
+            sure = {t for t in range(K) if w.M * sel.p[t] >= 1.0 + 1e-3}    # clear of near-ties
+            assert sure <= set(int(x) for x in teams[b, h] if x >= 0)
+    # Every head: sets ascending, unique, in range, at most min(M, K) teams.
+    for b in range(w.batch):
+        K = O.num_teams(int(w.seq_lens[b]), w.page_size)
+        for h in range(w.num_q_heads):
+            t = teams[b, h][teams[b, h] >= 0]
+            assert np.all(np.diff(t) > 0) and (len(t) == 0 or (t[0] >= 0 and t[-1] < K))
+            assert len(t) <= min(K, w.M)
+    assert np.all(np.isfinite(out))
