@@ -145,8 +145,8 @@ typedef enum santa_rep_kind {
  * full rebuild bit for bit. The new keys must already be in the pages and
  * kv->seq_lens must hold the new lengths.
  *   reps           as for santa_build_reps; rows of other teams untouched
- *   prev_seq_lens  [B] int32, device: lengths before the append, each <= the
- *                  new length (a smaller new length refreshes nothing)
+ *   prev_seq_lens  [B] int32, device: lengths before the append; a sequence
+ *                  whose length did not grow (prev >= new) keeps every row
  *   max_new_tokens host bound on the tokens appended to any one sequence
  *                  (>= 0; 0 enqueues nothing) */
 santa_status santa_update_reps(const santa_kv *kv, void *reps, const int32_t *prev_seq_lens,

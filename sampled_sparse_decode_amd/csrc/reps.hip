@@ -38,10 +38,12 @@ __global__ __launch_bounds__(kBlock) void build_reps_kernel(Params p) {
     const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int L = clamp_len(p.seq_lens[b], p.P * p.T);
     const int K = (L + p.T - 1) / p.T;
-    // Update mode: block x recomputes team first + x, first being the team
-    // that held the sequence's token prev_len (the first appended token).
-    const int first = p.prev_lens ? clamp_len(p.prev_lens[b], p.P * p.T) / p.T : 0;
-    const int t = first + blockIdx.x;
+    // Update mode: block x recomputes team prev / T + x, the first being the
+    // team that holds token prev (the first appended token); a sequence that
+    // did not grow keeps every row.
+    const int prev = p.prev_lens ? clamp_len(p.prev_lens[b], p.P * p.T) : 0;
+    if (p.prev_lens && prev >= L) return;      // nothing appended: no team changed
+    const int t = prev / p.T + blockIdx.x;
     if (t >= K) return;
     const int64_t page = clamp_page(p.page_table[size_t(b) * p.P + t], p.num_pages);
     const int n = min(p.T, L - t * p.T);
@@ -89,8 +91,9 @@ __device__ __forceinline__ bool team_of_block(const Params &p, TeamOfBlock &tm) 
     tm.b = blockIdx.z;
     const int L = clamp_len(p.seq_lens[tm.b], p.P * p.T);
     const int K = (L + p.T - 1) / p.T;
-    const int first = p.prev_lens ? clamp_len(p.prev_lens[tm.b], p.P * p.T) / p.T : 0;
-    tm.t = first + blockIdx.x;
+    const int prev = p.prev_lens ? clamp_len(p.prev_lens[tm.b], p.P * p.T) : 0;
+    if (p.prev_lens && prev >= L) return false;   // nothing appended: no team changed
+    tm.t = prev / p.T + blockIdx.x;
     if (tm.t >= K) return false;
     const int64_t page = clamp_page(p.page_table[size_t(tm.b) * p.P + tm.t], p.num_pages);
     tm.n = min(p.T, L - tm.t * p.T);

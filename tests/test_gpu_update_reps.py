@@ -66,3 +66,16 @@ def test_token_by_token_decode_keeps_reps_exact():
     torch.cuda.synchronize()
     assert np.array_equal(kv.seq_lens.cpu().numpy(), final)
     parity.check_reps(w, reps)
+
+
+def test_update_with_no_growth_writes_nothing():
+    # prev >= new length for every sequence (equal, or a rolled-back
+    # sequence): no team received tokens, so no row may change.
+    w = W.paged_ragged(num_seqs=3, len_min=300, len_max=900, T=32, M=8, hq=4, hkv=2, d=64)
+    print("[update_reps] no growth", flush=True)
+    kv, _ = S.kv_from_workload(w)
+    reps = _sentinel_reps(kv)
+    prev = torch.from_numpy((w.seq_lens + np.array([0, 5, 40])).astype(np.int32)).cuda()
+    S.santa_update_reps(kv, reps, prev, 64)
+    torch.cuda.synchronize()
+    assert np.all(reps.float().cpu().numpy() == -7.0)
