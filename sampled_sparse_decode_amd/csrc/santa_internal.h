@@ -1,5 +1,6 @@
 // Internal interface between the host entry points (santa_api.cpp) and the
-// HIP kernels (santa_kernels.hip). Not installed; not part of the C ABI.
+// HIP kernels (reps.hip, select.hip, gather.hip, pack.hip, cluster.hip).
+// Not installed; not part of the C ABI.
 #pragma once
 
 #include <stddef.h>
@@ -96,7 +97,7 @@ struct ClusterParams {
 // Host-side argument checks; no HIP calls.
 santa_status validate_kv(const santa_kv *kv);
 
-// Kernel launches (santa_kernels.hip). Each returns SANTA_OK or SANTA_ERR_HIP.
+// Kernel launches. Each returns SANTA_OK or SANTA_ERR_HIP.
 santa_status launch_build_reps(const Params &p, void *stream);
 santa_status launch_select(const Params &p, void *stream);
 santa_status launch_given(const Params &p, void *stream);
