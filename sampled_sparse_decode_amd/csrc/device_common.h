@@ -43,6 +43,15 @@ __device__ __forceinline__ uint4 ld16(const void *ptr) {
     return *reinterpret_cast<const uint4 *>(ptr);
 }
 
+// 16 bytes read once by the whole call (K/V tiles): a non-temporal load
+// (streaming cache policy), so the streamed tiles do not push other data out
+// of the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void *ptr) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ptr));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // float32 -> bfloat16 bits, round to nearest, ties to even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);

@@ -222,6 +222,9 @@ struct MfmaChunk {
     uint4 v[NT];
 };
 
+// K/V tiles are read once per call, with non-temporal loads (measured on
+// MI355X: gather 14.3 -> 13.2 us at 32K batch 1, 61.7 -> 55.9 us at batch 8,
+// 111 -> 105 us at 128K; the dense gather 181 -> 155 us at 128K).
 // Loads are unconditional: rows past the team's end are clamped to its last
 // valid row (K; those scores are masked) or to its first 8 tokens (V; zeroed
 // by keep_first), so every address stays inside the page and the wavefront
@@ -242,12 +245,12 @@ __device__ __forceinline__ void mfma_load_chunk_at(const Params &p, int64_t page
         const int tok = 8 * (i16 >> 2) + 4 * t + (i16 & 3);     // in-chunk token of this lane's row
         const bf16_t *row = kc + min(tok, max(n - 1 - tb, 0)) * 32 + 8 * g4;
 #pragma unroll
-        for (int ks = 0; ks < MfmaChunk<D>::KS; ++ks) c.k[t][ks] = ld16(row + ks * (C * 32));
+        for (int ks = 0; ks < MfmaChunk<D>::KS; ++ks) c.k[t][ks] = ld16_stream(row + ks * (C * 32));
     }
     const int tok0 = 8 * g4;
     const bf16_t *col = vc + i16 * C + (tb + tok0 < n ? tok0 : 0);
 #pragma unroll
-    for (int nt = 0; nt < MfmaChunk<D>::NT; ++nt) c.v[nt] = ld16(col + (16 * nt) * C);
+    for (int nt = 0; nt < MfmaChunk<D>::NT; ++nt) c.v[nt] = ld16_stream(col + (16 * nt) * C);
 }
 
 // Zero the bf16 elements e >= keep of a 16-byte operand (ragged team tails).

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kBlock) void build_reps_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < UNROLL; ++i) {
             const int r = r0 + i * RL;
-            v[i] = (r < n) ? ld16(keys + k_offset(r, ch * VPC, p.T, D)) : make_uint4(0, 0, 0, 0);
+            v[i] = (r < n) ? ld16_stream(keys + k_offset(r, ch * VPC, p.T, D)) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < UNROLL; ++i) {
