@@ -41,11 +41,15 @@ __device__ __forceinline__ int float_key(float f) {
 }
 __device__ __forceinline__ float key_float(int k) { return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff)); }
 
-template <typename KV, int D>
+// PIPE: request each scoring pass's representative rows before the previous
+// pass is scored (chosen by the host when the page table allows more than
+// one pass; same arithmetic either way).
+template <typename KV, int D, bool PIPE>
 __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     constexpr int VPC = KVTraits<KV>::kPerChunk;
     constexpr int CPP = D / VPC / kParts;          // 16-byte chunks per thread and row
     constexpr int ROWS = kSel / kParts;            // rows scored per pass
+    constexpr bool kPipe = PIPE && CPP <= 4;          // float32 rows at d = 128 do not fit the registers
     __shared__ double q_s[D];
     __shared__ double e_s[kMaxTeams];              // scores, then exp(s - m)
     __shared__ double c_s[kMaxTeams];              // cumulative sums of e within a wavefront's teams
@@ -83,11 +87,23 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     //    threads per row, two partial sums each, added in a fixed order. The
     //    float32-rounded maximum is gathered on the way (LDS atomic max).
     float mloc = -INFINITY;
-    for (int t = row0; t < ((K + ROWS - 1) / ROWS) * ROWS; t += ROWS) {
-        if (t != row0) {
+    const int tEnd = ((K + ROWS - 1) / ROWS) * ROWS;
+    for (int t = row0; t < tEnd; t += ROWS) {
+        if (!kPipe && t != row0) {
             const KV *r = reps + (size_t(t < K ? t : 0) * p.Hkv + g) * D + part * CPP * VPC;
 #pragma unroll
             for (int j = 0; j < CPP; ++j) raw[j] = ld16(r + j * VPC);
+        }
+        // The next pass's rows are requested before this pass is scored, so
+        // K > ROWS teams cost one memory latency, not one per pass (bfloat16
+        // rows; float32 rows would need more registers than 1024 threads have).
+        const bool more = t + ROWS < tEnd;                  // uniform over the block
+        uint4 nxt[CPP];
+        if (kPipe && more) {
+            const int tn = t + ROWS;
+            const KV *r = reps + (size_t(tn < K ? tn : 0) * p.Hkv + g) * D + part * CPP * VPC;
+#pragma unroll
+            for (int j = 0; j < CPP; ++j) nxt[j] = ld16(r + j * VPC);
         }
         double a0 = 0.0, a1 = 0.0;
 #pragma unroll
@@ -108,6 +124,10 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
         if (t < K) {
             if (part == 0) e_s[t] = sc;
             mloc = fmaxf(mloc, float(sc));
+        }
+        if (kPipe && more) {
+#pragma unroll
+            for (int j = 0; j < CPP; ++j) raw[j] = nxt[j];
         }
     }
     for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
@@ -293,12 +313,22 @@ __global__ __launch_bounds__(kBlock) void given_kernel(Params p) {
 santa_status launch_select(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(p.B * p.Hq);
+    const bool pipe = p.P > kSel / kParts;          // more than one scoring pass possible
     if (p.dtype == SANTA_BF16) {
-        if (p.d == 64) hipLaunchKernelGGL((select_kernel<bf16_t, 64>), grid, dim3(kSel), 0, st, p);
-        else hipLaunchKernelGGL((select_kernel<bf16_t, 128>), grid, dim3(kSel), 0, st, p);
+        if (p.d == 64) {
+            if (pipe) hipLaunchKernelGGL((select_kernel<bf16_t, 64, true>), grid, dim3(kSel), 0, st, p);
+            else hipLaunchKernelGGL((select_kernel<bf16_t, 64, false>), grid, dim3(kSel), 0, st, p);
+        } else {
+            if (pipe) hipLaunchKernelGGL((select_kernel<bf16_t, 128, true>), grid, dim3(kSel), 0, st, p);
+            else hipLaunchKernelGGL((select_kernel<bf16_t, 128, false>), grid, dim3(kSel), 0, st, p);
+        }
     } else {
-        if (p.d == 64) hipLaunchKernelGGL((select_kernel<float, 64>), grid, dim3(kSel), 0, st, p);
-        else hipLaunchKernelGGL((select_kernel<float, 128>), grid, dim3(kSel), 0, st, p);
+        if (p.d == 64) {
+            if (pipe) hipLaunchKernelGGL((select_kernel<float, 64, true>), grid, dim3(kSel), 0, st, p);
+            else hipLaunchKernelGGL((select_kernel<float, 64, false>), grid, dim3(kSel), 0, st, p);
+        } else {
+            hipLaunchKernelGGL((select_kernel<float, 128, false>), grid, dim3(kSel), 0, st, p);
+        }
     }
     return launched();
 }
