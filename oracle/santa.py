@@ -69,6 +69,17 @@ sums and for P(t in S) = pi_t; Monte Carlo convergence over seeds; the
 expected set size against its closed form; chi-square of draw frequencies
 against p; invariants (constant values, permuted page tables); team scores
 with one-token teams against the attention weights of the library routine.
+R9: the medoid of collinear keys is the median member (a skewed set
+separates it from the squared-distance choice), scipy's distance sums
+agree, ties go to the lowest index, translation invariance, outliers are
+never chosen; the random member is uniform (chi-square). R10: both
+inclusion probabilities equal an exact integration of the selection rule
+over its piecewise-constant pieces, the team sums stay unbiased, tiny teams
+keep full precision, equal teams give M distinct systematic draws, and on
+team-coherent keys both schemes lower the error. R11: code bits against
+basis directions, signs against exact rational dot products, a stable
+order that keeps separated clusters in one run, a per-head permutation
+that leaves dense attention unchanged, lower error on planted keys.
 """
 import math
 from fractions import Fraction
