@@ -60,8 +60,10 @@
  *   seq_lens          [batch] int32: cached tokens L_b of sequence b
  * A team is one page: team t of sequence b is tokens [t*T, min((t+1)*T, L_b))
  * stored in physical page page_table[b][t] (T = page_size). The pages leave
- * the team partition open ([EXP] 3.2); contiguous runs, one per page, is
- * this library's choice. Sequence b has K_b = ceil(L_b / T) teams.
+ * the team partition open ([EXP] 3.2); contiguous runs, one per page, are
+ * the default, and santa_pack_pages_hashed writes each sequence's tokens in
+ * a hash-partition order so that the same pages hold clustered teams.
+ * Sequence b has K_b = ceil(L_b / T) teams.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  */
 #ifndef SANTA_H
