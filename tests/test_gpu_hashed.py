@@ -91,3 +91,34 @@ def test_santa_and_dense_on_hashed_cache(name):
         for h in range(w.num_q_heads):
             parity.check_santa_head(wp, okv_p, ref_reps, b, h, out[b, h], lse[b, h], teams[b, h], inv_pi[b, h])
             parity.check_dense_head(w, okv, b, h, dout[b, h], dlse[b, h])   # the original order
+
+
+@pytest.mark.parametrize("name,pairs", [("qwen7b_32k_b1_m31", [(0, 0), (0, 20)]),
+                                        ("mixture_128k_b4_t256_m64", [(1, 5), (3, 26)])])
+def test_hashed_full_size(name, pairs):
+    # Full-size configurations: codes, order and pages of every sequence bit
+    # for bit; SANTA++ on the hashed cache for a sample of heads.
+    w = W.FULL_SIZE[name]()
+    K = max(1, -(-int(w.seq_lens.max()) // w.page_size))
+    bits = min(10, max(1, int(np.ceil(np.log2(K)))))
+    dirs = W.hash_directions(hkv=w.num_kv_heads, bits=bits, d=w.head_dim)
+    print(f"[hashed full] {name} bits={bits} heads={pairs}", flush=True)
+    kv, q, codes, token_of = S.kv_from_workload_hashed(w, dirs)
+    reps = S.santa_build_reps(kv)
+    out, lse, teams, inv_pi = S.santa_decode_attention(kv, q, reps, w.M, seed=w.seed, offset=w.offset,
+                                                       return_sets=True)
+    torch.cuda.synchronize()
+    k2, v2, codes_ref, tok_ref = O.cluster_pages(w.k_pages, w.v_pages, w.page_table, w.seq_lens, w.page_size,
+                                                 w.dtype, dirs)
+    assert np.array_equal(codes.cpu().numpy(), codes_ref)
+    assert np.array_equal(token_of.cpu().numpy(), tok_ref)
+    wp = W.permuted_workload(w, k2, v2)
+    kvp, _ = S.kv_from_workload(wp)
+    used = _used_pages(w).to(kv.device)
+    assert torch.equal(kv.k_pages[used], kvp.k_pages[used]) and torch.equal(kv.v_pages[used], kvp.v_pages[used])
+    del kvp
+    ref_reps = parity.check_reps(wp, reps, pairs)
+    okv = parity.oracle_kv(wp)
+    out, lse, teams, inv_pi = (x.cpu().numpy() for x in (out, lse, teams, inv_pi))
+    for b, h in pairs:
+        parity.check_santa_head(wp, okv, ref_reps, b, h, out[b, h], lse[b, h], teams[b, h], inv_pi[b, h])

@@ -114,3 +114,27 @@ def test_santa_decode_on_medoid_reps_matches_oracle(dtype):
     for b in range(w.batch):
         for h in range(w.num_q_heads):
             parity.check_santa_head(w, okv, ref_reps, b, h, out[b, h], lse[b, h], sampled[b, h], inv_pi[b, h])
+
+
+@pytest.mark.parametrize("kind", ["medoid", "random"])
+def test_reps_kind_full_size_sampled_teams(kind):
+    # The 128K configuration (T = 256, d = 128): every representative row is
+    # a member of its team, and a sample of (sequence, team, KV head) rows
+    # equals the oracle's choice.
+    w = W.FULL_SIZE["mixture_128k_b4_t256_m64"]()
+    print(f"[reps_kind full] {kind}", flush=True)
+    kv, _ = S.kv_from_workload(w)
+    reps = S.santa_build_reps_ex(kv, kind, seed=21)
+    torch.cuda.synchronize()
+    got = parity.decoded_reps(reps, w.dtype)
+    rng = np.random.default_rng(4)
+    T = w.page_size
+    for _ in range(12):
+        b = int(rng.integers(0, w.batch))
+        K = O.num_teams(int(w.seq_lens[b]), T)
+        t = int(rng.integers(0, K))
+        g = int(rng.integers(0, w.num_kv_heads))
+        n = O.team_size(int(w.seq_lens[b]), T, t)
+        keys = O.decode(w.k_pages[int(w.page_table[b][t]), g, :n, :], w.dtype)
+        i = O.team_medoid_index(keys) if kind == "medoid" else O.team_random_index(n, 21, b, t, g)
+        assert np.array_equal(got[b, t, g], keys[i]), f"{kind}: (b={b}, t={t}, g={g}) differs from the oracle"
