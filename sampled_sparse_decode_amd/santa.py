@@ -255,6 +255,7 @@ def santa_build_reps(kv, reps=None):
     if reps is None:
         reps = torch.zeros((kv.batch, kv.max_pages_per_seq, kv.num_kv_heads, kv.head_dim), dtype=kv.dtype,
                            device=kv.device)
+    _check_reps(kv, reps)
     d = kv.desc()
     _check("santa_build_reps", load().santa_build_reps(ctypes.byref(d), _ptr(reps), _stream()))
     return reps
@@ -265,6 +266,7 @@ def santa_update_reps(kv, reps, prev_seq_lens, max_new_tokens):
     sequence lengths were ``prev_seq_lens`` (device int32 [B])."""
     if prev_seq_lens.dtype != torch.int32 or tuple(prev_seq_lens.shape) != (kv.batch,):
         raise ValueError("prev_seq_lens must be an int32 [B] tensor")
+    _check_reps(kv, reps)
     d = kv.desc()
     _check("santa_update_reps", load().santa_update_reps(ctypes.byref(d), _ptr(reps), _ptr(prev_seq_lens),
                                                         int(max_new_tokens), _stream()))
@@ -288,6 +290,7 @@ def santa_build_reps_ex(kv, kind, reps=None, seed=0, prev_seq_lens=None, max_new
     if prev_seq_lens is not None and (prev_seq_lens.dtype != torch.int32
                                       or tuple(prev_seq_lens.shape) != (kv.batch,)):
         raise ValueError("prev_seq_lens must be an int32 [B] tensor")
+    _check_reps(kv, reps)
     d = kv.desc()
     _check("santa_build_reps_ex",
            load().santa_build_reps_ex(ctypes.byref(d), _ptr(reps), code, int(seed) & (2**64 - 1),
@@ -296,9 +299,42 @@ def santa_build_reps_ex(kv, kind, reps=None, seed=0, prev_seq_lens=None, max_new
     return reps
 
 
+def _check_tensor(name, t, shape, dtype, device):
+    """A caller-provided buffer must match exactly: the library reads and
+    writes through its pointer with the sizes of the cache descriptor."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _check_reps(kv, reps):
+    if reps is None:
+        raise ValueError("reps is required")
+    _check_tensor("reps", reps, (kv.batch, kv.max_pages_per_seq, kv.num_kv_heads, kv.head_dim), kv.dtype, kv.device)
+
+
+def _check_outputs(kv, out=None, lse=None):
+    _check_tensor("out", out, (kv.batch, kv.num_q_heads, kv.head_dim), torch.float32, kv.device)
+    _check_tensor("lse", lse, (kv.batch, kv.num_q_heads), torch.float32, kv.device)
+
+
+def _check_sets(kv, M, sampled, inv_pi):
+    _check_tensor("sampled", sampled, (kv.batch, kv.num_q_heads, int(M)), torch.int32, kv.device)
+    _check_tensor("inv_pi", inv_pi, (kv.batch, kv.num_q_heads, int(M)), torch.float32, kv.device)
+
+
+def _check_workspace(workspace, kv):
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()
+                                  or workspace.device != kv.device):
+        raise ValueError("workspace must be a contiguous uint8 tensor on the cache's device")
+
+
 def _check_q(kv, q):
-    if q.dtype != kv.dtype or not q.is_contiguous() or tuple(q.shape) != (kv.batch, kv.num_q_heads, kv.head_dim):
-        raise ValueError("q must be a contiguous [B][Hq][d] tensor of the cache dtype")
+    if (q.dtype != kv.dtype or not q.is_contiguous() or tuple(q.shape) != (kv.batch, kv.num_q_heads, kv.head_dim)
+            or q.device != kv.device):
+        raise ValueError("q must be a contiguous [B][Hq][d] tensor of the cache dtype on the cache's device")
 
 
 DRAW_IID, DRAW_SYSTEMATIC, DRAW_STRATIFIED = 0, 1, 2
@@ -327,6 +363,9 @@ def santa_decode_attention_ex(kv, q, reps, M, scheme, seed=0, offset=0, workspac
 
 def _decode(kv, q, reps, M, seed, offset, scheme, workspace, out, lse, return_sets):
     _check_q(kv, q)
+    _check_reps(kv, reps)
+    _check_outputs(kv, out, lse)
+    _check_workspace(workspace, kv)
     B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
     dev = kv.device
     if workspace is None:
@@ -358,6 +397,9 @@ def _decode(kv, q, reps, M, seed, offset, scheme, workspace, out, lse, return_se
 def santa_select_teams(kv, q, reps, M, seed, offset, workspace, sampled=None, inv_pi=None):
     """Steps 1-4 of SANTA++ into ``workspace`` (and sampled / inv_pi when given)."""
     _check_q(kv, q)
+    _check_reps(kv, reps)
+    _check_sets(kv, M, sampled, inv_pi)
+    _check_workspace(workspace, kv)
     desc = kv.desc()
     st = load().santa_select_teams(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed), int(offset),
                                    _ptr(sampled), _ptr(inv_pi), _ptr(workspace), workspace.numel(), _stream())
@@ -367,6 +409,9 @@ def santa_select_teams(kv, q, reps, M, seed, offset, workspace, sampled=None, in
 def santa_select_teams_ex(kv, q, reps, M, scheme, seed, offset, workspace, sampled=None, inv_pi=None):
     """santa_select_teams with a draw scheme: "iid", "systematic" or "stratified"."""
     _check_q(kv, q)
+    _check_reps(kv, reps)
+    _check_sets(kv, M, sampled, inv_pi)
+    _check_workspace(workspace, kv)
     desc = kv.desc()
     st = load().santa_select_teams_ex(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed), int(offset),
                                       _scheme_code(scheme), _ptr(sampled), _ptr(inv_pi), _ptr(workspace),
@@ -377,6 +422,8 @@ def santa_select_teams_ex(kv, q, reps, M, scheme, seed, offset, workspace, sampl
 def santa_attend_selected(kv, q, M, workspace, out, lse=None):
     """Step 5 of SANTA++ over the teams the last santa_select_teams left in ``workspace``."""
     _check_q(kv, q)
+    _check_outputs(kv, out, lse)
+    _check_workspace(workspace, kv)
     desc = kv.desc()
     st = load().santa_attend_selected(ctypes.byref(desc), _ptr(q), int(M), _ptr(out), _ptr(lse),
                                       _ptr(workspace), workspace.numel(), _stream())
@@ -387,6 +434,8 @@ def santa_attend_selected(kv, q, M, workspace, out, lse=None):
 def dense_decode_attention(kv, q, workspace=None, out=None, lse=None):
     """Dense decode attention over every cached token. Returns (out, lse)."""
     _check_q(kv, q)
+    _check_outputs(kv, out, lse)
+    _check_workspace(workspace, kv)
     B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
     if workspace is None:
         workspace = make_workspace(kv, 1)
@@ -404,6 +453,8 @@ def dense_decode_attention(kv, q, workspace=None, out=None, lse=None):
 def santa_attention_given_teams(kv, q, teams, weights, workspace=None, out=None, lse=None):
     """Estimator over caller-chosen teams [B][Hq][M] (int32, -1 unused) and weights (float32)."""
     _check_q(kv, q)
+    _check_outputs(kv, out, lse)
+    _check_workspace(workspace, kv)
     B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
     M = int(teams.shape[-1])
     if teams.dtype != torch.int32 or weights.dtype != torch.float32 or tuple(teams.shape) != (B, Hq, M) \

@@ -204,3 +204,33 @@ def test_pack_pages_hashed_validation(lib):
     assert call(ctypes.byref(k), F, far2, F, 4, F, F, None) == SHAPE          # source overlaps destination
     assert call(ctypes.byref(kv()), far, far2, F, 4, F, F, None) == SHAPE     # destinations overlap
     assert call(ctypes.byref(kv(head_dim=80)), far, far2, F, 4, F, F, None) == UNSUP
+
+
+def test_binding_rejects_mismatched_buffers():
+    """The binding checks caller-provided tensors against the cache
+    descriptor before any library call (no GPU needed: CPU tensors)."""
+    import torch
+    B, P, Hkv, G, T, d = 2, 4, 2, 3, 16, 64
+    kv = S.KVCache(torch.zeros((8, Hkv, T * d), dtype=torch.bfloat16), torch.zeros((8, Hkv, T * d), dtype=torch.bfloat16),
+                   torch.zeros((B, P), dtype=torch.int32), torch.zeros((B,), dtype=torch.int32), Hkv * G, T)
+    q = torch.zeros((B, Hkv * G, d), dtype=torch.bfloat16)
+    good = torch.zeros((B, P, Hkv, d), dtype=torch.bfloat16)
+    for bad in (torch.zeros((B, P, Hkv, d), dtype=torch.float32), torch.zeros((B, P + 1, Hkv, d), dtype=torch.bfloat16),
+                torch.zeros((B, P, Hkv, 2 * d), dtype=torch.bfloat16)[..., ::2]):
+        with pytest.raises(ValueError):
+            S.santa_decode_attention(kv, q, bad, 4)
+        with pytest.raises(ValueError):
+            S.santa_build_reps(kv, bad)
+        with pytest.raises(ValueError):
+            S.santa_update_reps(kv, bad, torch.zeros((B,), dtype=torch.int32), 1)
+        with pytest.raises(ValueError):
+            S.santa_build_reps_ex(kv, "medoid", reps=bad)
+    with pytest.raises(ValueError):
+        S.santa_decode_attention(kv, q, good, 4, out=torch.zeros((B, Hkv * G, d + 1)))
+    with pytest.raises(ValueError):
+        S.santa_decode_attention(kv, q, good, 4, lse=torch.zeros((B, Hkv * G), dtype=torch.float64))
+    with pytest.raises(ValueError):
+        S.santa_select_teams(kv, q, good, 4, 0, 0, torch.zeros(16, dtype=torch.uint8),
+                             torch.zeros((B, Hkv * G, 5), dtype=torch.int32), torch.zeros((B, Hkv * G, 5)))
+    with pytest.raises(ValueError):
+        S.dense_decode_attention(kv, q, torch.zeros(16, dtype=torch.float32))
