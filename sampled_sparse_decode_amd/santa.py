@@ -186,6 +186,10 @@ def santa_pack_pages_hashed(kv, k_src, v_src, directions, codes=None, token_of=N
             or directions.shape[0] != kv.num_kv_heads or directions.shape[2] != kv.head_dim):
         raise ValueError("directions must be a contiguous float32 [Hkv][bits][d] tensor")
     shape = (kv.batch, kv.num_kv_heads, kv.max_pages_per_seq * kv.page_size)
+    _check_tensor("codes", codes, shape, torch.int32, kv.device)
+    _check_tensor("token_of", token_of, shape, torch.int32, kv.device)
+    if directions.device != kv.device or k_src.device != kv.device or v_src.device != kv.device:
+        raise ValueError("k_src, v_src and directions must be on the cache's device")
     if codes is None:
         codes = torch.empty(shape, dtype=torch.int32, device=kv.device)
     if token_of is None:
