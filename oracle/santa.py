@@ -61,6 +61,16 @@ Readings taken where the pages leave a step open (each repeated where used):
       sorted by code and cut into runs of T, so team t holds sorted
       positions tT .. tT + T - 1 (the last team may be short). The cache
       is rewritten in that order, so every other step is unchanged.
+  R12 k-means-partitioned teams (the "cluster" partition of the same
+      passages). Per (sequence, KV head) with L tokens and C clusters:
+      centroids start at the keys of tokens floor(c L / C); each iteration
+      assigns every token to argmax_c (k . mu_c - |mu_c|^2 / 2) (the nearest
+      centroid; lowest c on ties), both terms float64 sums in channel order
+      of separately rounded products, then moves each non-empty cluster's
+      centroid to the float64 mean of its members (sums in token order, one
+      divide); after `iters` assignments (no move after the last) the
+      assignment is the code, and the tokens are stably sorted by code and
+      cut into runs of T as in R11.
 
 Parity pins (tests/test_oracle_pins.py): dense attention against torch's
 scaled_dot_product_attention; full coverage against dense; brute-force
@@ -245,6 +255,70 @@ def cluster_pages(k_pages, v_pages, page_table, seq_lens, page_size, dtype, dire
             keys = k_pages[pages, g].reshape(K * T, d)[:L]
             vals = v_pages[pages, g].reshape(K * T, d)[:L]
             c = hash_codes(decode(keys, dtype), directions[g])
+            order = np.argsort(c, kind="stable")
+            codes[b, g, :L] = c
+            token_of[b, g, :L] = order
+            nk = np.zeros((K * T, d), dtype=k_pages.dtype)
+            nv = np.zeros((K * T, d), dtype=v_pages.dtype)
+            nk[:L] = keys[order]
+            nv[:L] = vals[order]
+            k2[pages, g] = nk.reshape(K, T, d)
+            v2[pages, g] = nv.reshape(K, T, d)
+    return k2, v2, codes, token_of
+
+
+def kmeans_codes(keys, clusters, iters):
+    """Cluster of each key [L][d] after `iters` k-means assignments (R12).
+
+    Plain loops in the orders R12 fixes, vectorised over tokens and
+    clusters only: every product is rounded before it is added.
+    """
+    x = np.asarray(keys, dtype=np.float64)
+    L, d = x.shape
+    C = int(clusters)
+    mu = x[[(c * L) // C for c in range(C)]].copy()          # [C][d]
+    assign = np.zeros(L, dtype=np.int64)
+    for it in range(int(iters)):
+        half = np.zeros(C)
+        for ch in range(d):
+            half = half + mu[:, ch] * mu[:, ch]
+        for i0 in range(0, L, 1024):                          # token blocks (same arithmetic per element)
+            xb = x[i0:i0 + 1024]
+            dot = np.zeros((len(xb), C))
+            for ch in range(d):
+                dot = dot + xb[:, ch:ch + 1] * mu[None, :, ch]
+            assign[i0:i0 + 1024] = np.argmax(dot - half[None, :] / 2.0, axis=1)   # lowest c on ties
+        if it + 1 < int(iters):
+            for c in range(C):
+                members = np.nonzero(assign == c)[0]          # token order
+                if len(members) == 0:
+                    continue
+                # running sum from +0.0, one row at a time, in token order
+                acc = np.add.accumulate(np.vstack([np.zeros((1, d)), x[members]]), axis=0)[-1]
+                mu[c] = acc / len(members)
+    return assign
+
+
+def cluster_pages_kmeans(k_pages, v_pages, page_table, seq_lens, page_size, dtype, clusters, iters):
+    """The cache rewritten in k-means order (R12); same outputs as
+    cluster_pages. `clusters` is per sequence: a number, or None for one
+    cluster per team (K_b)."""
+    _, hkv, T, d = k_pages.shape
+    B, P = np.asarray(page_table).shape
+    k2, v2 = k_pages.copy(), v_pages.copy()
+    codes = np.full((B, hkv, P * T), -1, dtype=np.int64)
+    token_of = np.full((B, hkv, P * T), -1, dtype=np.int64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        K = num_teams(L, T)
+        if L == 0:
+            continue
+        C = min(L, K if clusters is None else int(clusters))
+        pages = np.asarray(page_table[b][:K], dtype=np.int64)
+        for g in range(hkv):
+            keys = k_pages[pages, g].reshape(K * T, d)[:L]
+            vals = v_pages[pages, g].reshape(K * T, d)[:L]
+            c = kmeans_codes(decode(keys, dtype), C, iters)
             order = np.argsort(c, kind="stable")
             codes[b, g, :L] = c
             token_of[b, g, :L] = order

@@ -658,3 +658,72 @@ def test_hash_teams_lower_the_error_on_planted_tokens():
                 err.append(np.sum((r.out - out_d) ** 2))
         mse[name] = np.mean(err)
     assert mse["hashed"] < 0.5 * mse["contiguous"]
+
+
+# --------------------------------------------------------------------------
+# k-means-partitioned teams (reading R12)
+# --------------------------------------------------------------------------
+
+def test_kmeans_matches_scikit_learn_lloyd():
+    # Same start (the keys of tokens floor(c L / C)), iters assignments with
+    # iters - 1 centroid moves in between: scikit-learn's Lloyd k-means with
+    # max_iter = iters - 1 ends with the same labels (its final E-step makes
+    # them consistent with the last centres). Data without near ties.
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(60)
+    for L, d, C, iters in ((600, 16, 6, 4), (900, 32, 12, 3), (256, 8, 4, 6)):
+        centres = rng.standard_normal((C, d)) * 3.0
+        x = centres[rng.integers(0, C, L)] + rng.standard_normal((L, d))
+        init = x[[(c * L) // C for c in range(C)]]
+        km = KMeans(n_clusters=C, init=init, n_init=1, max_iter=iters - 1, algorithm="lloyd", tol=0.0).fit(x)
+        assert np.array_equal(santa.kmeans_codes(x, C, iters), km.labels_)
+
+
+def test_kmeans_recovers_separated_runs():
+    # C runs of equal length, far apart: the evenly spaced start puts one
+    # centroid in each run, and every token keeps its run's label.
+    rng = np.random.default_rng(61)
+    C, n, d = 5, 40, 16
+    centres = rng.standard_normal((C, d)) * 20.0
+    x = np.repeat(centres, n, axis=0) + 0.1 * rng.standard_normal((C * n, d))
+    assert np.array_equal(santa.kmeans_codes(x, C, 3), np.repeat(np.arange(C), n))
+
+
+def test_kmeans_objective_never_rises_and_ties_go_low():
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal((500, 12))
+    C = 7
+    costs = []
+    for iters in range(1, 7):
+        a = santa.kmeans_codes(x, C, iters)
+        mu = np.array([x[a == c].mean(axis=0) if np.any(a == c) else np.zeros(12) for c in range(C)])
+        costs.append(float(np.sum((x - mu[a]) ** 2)))
+    assert all(costs[i + 1] <= costs[i] + 1e-9 for i in range(len(costs) - 1))
+    # Two identical starting centroids (centroids come from tokens 0, 2, 4,
+    # 6, 8; tokens 0 and 2 are made equal): cluster 1 always ties with
+    # cluster 0 and is never chosen.
+    y = x[:10].copy()
+    y[2] = y[0]
+    a = santa.kmeans_codes(y, 5, 1)
+    assert not np.any(a == 1) and a[2] == 0
+
+
+def test_cluster_pages_kmeans_is_a_permutation_that_keeps_dense_attention():
+    w = wl.gaussian_mixture(batch=2, seq_len=700, T=32, M=8, hq=4, hkv=2, d=32, components=6, run_min=1,
+                            run_max=12)
+    k2, v2, codes, tok = santa.cluster_pages_kmeans(w.k_pages, w.v_pages, w.page_table, w.seq_lens, w.page_size,
+                                                    w.dtype, None, 3)
+    kv0, kv1 = _kv(w), santa.PagedKV(w.dtype, k2, v2, w.page_table, w.seq_lens)
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        for g in range(2):
+            k0, v0 = kv0.all_tokens(b, g)
+            k1, v1 = kv1.all_tokens(b, g)
+            order = tok[b, g, :L]
+            assert np.array_equal(k1, k0[order]) and np.array_equal(v1, v0[order])
+            assert np.all(np.diff(codes[b, g, order]) >= 0)
+        for h in range(4):
+            qh = numerics.decode(w.q[b, h], w.dtype)
+            o0, l0 = santa.dense_head(kv0, qh, b, h, 4)
+            o1, l1 = santa.dense_head(kv1, qh, b, h, 4)
+            assert np.max(np.abs(o0 - o1)) < 1e-12 and abs(l0 - l1) < 1e-12
