@@ -52,7 +52,7 @@ def parse():
                     help="workloads also measured, compactly, after the headline one ('' = none)")
     ap.add_argument("--scale-steps", type=int, default=100)
     ap.add_argument("--no-extras", action="store_true",
-                    help="time only the decode path (no draw schemes, hashed teams or representative builds)")
+                    help="time only the decode path (no draw schemes, hashed or k-means teams or representative builds)")
     return ap.parse_args()
 
 
@@ -254,7 +254,7 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
     torch.cuda.synchronize()
     r["attend_us"], _ = median_graph(attend_step, R, steps, warmup, torch)
 
-    r["schemes"], r["hashed"] = None, None
+    r["schemes"], r["hashed"], r["kmeans"] = None, None, None
     if extras:
         # The variance-reduced draw schemes: whole decode call, and the bytes of
         # their (larger: fewer repeated teams) unions.
@@ -274,21 +274,40 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
                                   "kv_read_fraction": {"per_query_head": round(abs_["frac_head"], 4),
                                                        "hbm": round(abs_["frac_hbm"], 4)}}
 
-        # Hash-partitioned teams: the pack that writes them (from plain pages),
-        # SANTA++ on them, their bytes, and the estimate's error against dense
-        # attention for contiguous and hashed teams (mean over heads of
-        # ||out - dense|| / ||dense||, over 16 draw offsets).
+        # Re-partitioned teams (sign-hash and k-means): the pack that writes
+        # them (from plain pages), SANTA++ on them, their bytes, and the
+        # estimate's error against dense attention for contiguous, hashed and
+        # k-means teams (mean over heads of ||out - dense|| / ||dense||, over
+        # 16 draw offsets).
         from sampled_sparse_decode_amd import workloads as W
         K = max(1, -(-int(w.seq_lens.max()) // w.page_size))
         bits = min(10, max(1, math.ceil(math.log2(K))))
         dirs = torch.from_numpy(W.hash_directions(hkv=w.num_kv_heads, bits=bits, d=w.head_dim)).to(dev)
         k_src = S.storage_tensor(w.k_pages, w.dtype, dev)
         v_src = S.storage_tensor(w.v_pages, w.dtype, dev)
-        hcache = [S.KVCache(torch.empty_like(kv.k_pages), torch.empty_like(kv.v_pages), kv.page_table, kv.seq_lens,
-                            w.num_q_heads, w.page_size) for kv in cache]
         codes = torch.empty((w.batch, w.num_kv_heads, w.max_pages_per_seq * w.page_size), dtype=torch.int32,
                             device=dev)
         token_of = torch.empty_like(codes)
+
+        def fresh_caches():
+            return [S.KVCache(torch.empty_like(kv.k_pages), torch.empty_like(kv.v_pages), kv.page_table,
+                              kv.seq_lens, w.num_q_heads, w.page_size) for kv in cache]
+
+        def santa_on(pcache):
+            preps = [S.santa_build_reps(kv) for kv in pcache]
+            _, _, smp, _ = S.santa_decode_attention(pcache[0], q, preps[0], M, w.seed, w.offset, wss[0],
+                                                    return_sets=True)
+            torch.cuda.synchronize()
+            abp = algorithmic_bytes(w, union_stats(w, smp.cpu().numpy()))
+
+            def step(i):
+                j = i % R
+                S.santa_decode_attention(pcache[j], q, preps[j], M, w.seed, w.offset, wss[j], out, lse)
+
+            us, _ = median_graph(step, R, steps, warmup, torch)
+            return preps, us, {"per_query_head": round(abp["frac_head"], 4), "hbm": round(abp["frac_hbm"], 4)}
+
+        hcache = fresh_caches()
 
         def hpack_step(i):
             S.santa_pack_pages_hashed(hcache[i % R], k_src, v_src, dirs, codes, token_of)
@@ -296,28 +315,41 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
         hp_us, _ = median_graph(hpack_step, R, max(R, steps // 4), max(R, warmup // 4), torch)
         for j in range(R):
             hpack_step(j)
-        del k_src, v_src
-        hreps = [S.santa_build_reps(kv) for kv in hcache]
-        _, _, smp, _ = S.santa_decode_attention(hcache[0], q, hreps[0], M, w.seed, w.offset, wss[0], return_sets=True)
+        hreps, hs_us, hfrac = santa_on(hcache)
+
+        # k-means: one cluster per team, 10 assignments; the pack is timed
+        # eagerly over a few calls (it is milliseconds long).
+        km_iters = 10
+        kcache = fresh_caches()
+        kws = torch.empty(S.santa_kmeans_workspace_size(kcache[0], 0), dtype=torch.uint8, device=dev)
+        for j in range(R):
+            S.santa_pack_pages_kmeans(kcache[j], k_src, v_src, 0, km_iters, codes, token_of, kws)
         torch.cuda.synchronize()
-        abh = algorithmic_bytes(w, union_stats(w, smp.cpu().numpy()))
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for j in range(3):
+            S.santa_pack_pages_kmeans(kcache[j % R], k_src, v_src, 0, km_iters, codes, token_of, kws)
+        ev1.record()
+        torch.cuda.synchronize()
+        kp_us = ev0.elapsed_time(ev1) * 1000.0 / 3
+        del k_src, v_src, kws
+        kreps, ks_us, kfrac = santa_on(kcache)
 
-        def hsanta_step(i):
-            j = i % R
-            S.santa_decode_attention(hcache[j], q, hreps[j], M, w.seed, w.offset, wss[j], out, lse)
-
-        hs_us, _ = median_graph(hsanta_step, R, steps, warmup, torch)
         dense_out, _ = S.dense_decode_attention(kv0, q, wss[0])
-        errs = {"contiguous": [], "hashed": []}
+        errs = {"contiguous": [], "hashed": [], "kmeans": []}
         for off in range(16):
-            for name, kv, rp in (("contiguous", kv0, reps[0]), ("hashed", hcache[0], hreps[0])):
+            for name, kv, rp in (("contiguous", kv0, reps[0]), ("hashed", hcache[0], hreps[0]),
+                                 ("kmeans", kcache[0], kreps[0])):
                 o, _ = S.santa_decode_attention(kv, q, rp, M, w.seed, w.offset + 1000 + off, wss[0])
                 errs[name].append(((o - dense_out).norm(dim=-1) / dense_out.norm(dim=-1)).mean().item())
+        rel = {k: round(float(np.mean(v)), 4) for k, v in errs.items()}
         r["hashed"] = {"bits": bits, "pack_us": round(hp_us, 2), "santa_us_per_layer": round(hs_us, 3),
-                       "kv_read_fraction": {"per_query_head": round(abh["frac_head"], 4),
-                                            "hbm": round(abh["frac_hbm"], 4)},
-                       "estimate_rel_error": {k: round(float(np.mean(v)), 4) for k, v in errs.items()}}
-        del hcache, hreps
+                       "kv_read_fraction": hfrac,
+                       "estimate_rel_error": {"contiguous": rel["contiguous"], "hashed": rel["hashed"]}}
+        r["kmeans"] = {"clusters_per_seq": "one per team", "iters": km_iters, "pack_us": round(kp_us, 1),
+                       "santa_us_per_layer": round(ks_us, 3), "kv_read_fraction": kfrac,
+                       "estimate_rel_error": {"contiguous": rel["contiguous"], "kmeans": rel["kmeans"]}}
+        del hcache, hreps, kcache, kreps
 
     # Representative upkeep of one decode step: every sequence's last token is
     # taken as just appended (lengths one less before), its team refreshed.
@@ -401,6 +433,7 @@ def main():
         "build_reps_us": {k: round(v, 2) for k, v in r["build_reps_us"].items()},
         "draw_schemes": r["schemes"],
         "hashed_teams": r["hashed"],
+        "kmeans_teams": r["kmeans"],
         "roofline": {"kernel": "gather+combine (santa_attend_selected)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
@@ -421,7 +454,7 @@ def main():
                        "kv_read_fraction_hbm": round(a["frac_hbm"], 4),
                        "build_reps_us": {k: round(v, 2) for k, v in rs["build_reps_us"].items()},
                        "draw_schemes": rs["schemes"],
-                       "hashed_teams": rs["hashed"]}
+                       "hashed_teams": rs["hashed"], "kmeans_teams": rs["kmeans"]}
         del ws
         torch.cuda.empty_cache()
     if scale:

@@ -320,6 +320,42 @@ santa_status santa_pack_pages_hashed(const santa_kv *kv, const void *k_src, cons
                                      const float *directions, int32_t bits,
                                      int32_t *codes, int32_t *token_of, void *stream);
 
+/* k-means-partitioned teams ([EXP] section 三 step 1: teams are clusters of
+ * keys; section 八 pitfall 3: the clustering is a choice). Like
+ * santa_pack_pages_hashed, but the codes are cluster ids from Lloyd's
+ * k-means on the keys of each (sequence b, KV head g):
+ *   C_b = min(L_b, clusters), or min(L_b, K_b) when clusters is 0 (one
+ *         cluster per team on average);
+ *   start: centroid c = the key of token floor(c L_b / C_b);
+ *   assign: token i goes to the c with the largest k_i . mu_c - |mu_c|^2 / 2
+ *         (the nearest centroid), lowest c on ties; both terms are float64
+ *         sums in channel order of separately rounded float64 products;
+ *   move: each non-empty cluster's centroid becomes the float64 mean of its
+ *         keys, summed in token order from +0.0 and divided once; an empty
+ *         cluster's centroid stays;
+ *   `iters` assignments with a move between consecutive ones; the codes are
+ *         those of the last assignment.
+ * Tokens are then stably sorted by code and written to the teams as for the
+ * hash partition. Non-finite keys give a valid permutation but no defined
+ * clustering.
+ *   kv, k_src, v_src, codes, token_of   as for santa_pack_pages_hashed
+ *               (codes are cluster ids in [0, C_b))
+ *   clusters    0, or the clusters per sequence; clusters (or
+ *               max_pages_per_seq when 0), capped at max_pages_per_seq * T,
+ *               must be <= 1024
+ *   iters       1 .. 1000
+ *   workspace   device buffer of santa_kmeans_workspace_size bytes, 8-byte
+ *               aligned; holds the centroids and sort offsets; no
+ *               initialisation needed, meaningless afterwards
+ * Errors: SANTA_ERR_NULL, SANTA_ERR_SHAPE (sizes, clusters, iters,
+ * overlapping source and destination), SANTA_ERR_WORKSPACE, and the
+ * validation statuses of the cache. Enqueues 3 * iters + 1 launches. */
+santa_status santa_kmeans_workspace_size(const santa_kv *kv, int32_t clusters, size_t *bytes);
+santa_status santa_pack_pages_kmeans(const santa_kv *kv, const void *k_src, const void *v_src,
+                                     int32_t clusters, int32_t iters, int32_t *codes,
+                                     int32_t *token_of, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 /* Static description of a status code. */
 const char *santa_status_string(int32_t status);
 

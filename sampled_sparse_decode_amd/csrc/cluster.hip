@@ -132,6 +132,11 @@ __global__ __launch_bounds__(kSortThreads) void hash_rank_kernel(ClusterParams c
     __syncthreads();
     int base = incl - total;
     for (int w = 0; w < wave; ++w) base += wsum[w];
+    if (c.starts && tid < nb) {
+        int32_t *st = c.starts + (size_t(b) * c.Hkv + g) * (nb + 1);
+        st[tid] = base;
+        if (tid == nb - 1) st[nb] = L;
+    }
     if (tid < nb) {
         for (int w = 0; w < kSortWaves; ++w) {
             const int n = hist[w][tid];
@@ -226,6 +231,171 @@ __global__ __launch_bounds__(kBlock) void pack_hashed_kernel(ClusterParams c) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// k-means-partitioned teams: the codes are cluster ids from Lloyd iterations
+// on the keys of each (sequence, KV head); the stable sort and the permuted
+// pack above then lay the teams out as for the hash partition.
+//
+// [EXP] section 三 step 1 (teams are clusters of keys) and section 八
+// pitfall 3 (the clustering is a choice). Lloyd's iteration (assign every
+// key to its nearest centroid, move each centroid to the mean of its keys)
+// is the textbook k-means; the steps the pages leave open are fixed as
+// follows. C_b = min(L_b, clusters, or K_b when clusters is 0) clusters start
+// at the keys of tokens floor(c L_b / C_b). Nearest means the largest
+// k . mu_c - |mu_c|^2 / 2 (the same order as the smallest distance), both
+// terms float64 sums in channel order of separately rounded products, ties
+// to the lowest c. A non-empty cluster moves to the float64 mean of its keys
+// summed in token order from +0.0; an empty one stays. `iters` assignments,
+// with a move between consecutive ones. Every sum and product is rounded as
+// written (contraction off), so the partition is reproducible bit for bit.
+
+__device__ __forceinline__ int kmeans_clusters(const ClusterParams &c, int L) {
+    const int K = (L + c.T - 1) / c.T;
+    const int want = c.clusters > 0 ? c.clusters : K;
+    return min(L, min(want, c.cmax));
+}
+
+// Centroid k of (b, g) from one channel per thread (D threads): stored, and
+// its squared norm summed in channel order by thread 0.
+template <int D>
+__device__ __forceinline__ void store_centroid(const ClusterParams &c, int b, int g, int k, double m,
+                                               double *m_s) {
+#pragma clang fp contract(off)
+    const size_t row = (size_t(b) * c.Hkv + g) * size_t(c.cmax) + k;
+    c.mu[row * D + threadIdx.x] = m;
+    m_s[threadIdx.x] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double h = 0.0;
+        for (int ch = 0; ch < D; ++ch) h = h + m_s[ch] * m_s[ch];
+        c.half[row] = h;
+    }
+}
+
+// 1. Start: centroid k = the key of token floor(k L / C).
+template <typename KV, int D>
+__global__ __launch_bounds__(D) void kmeans_init_kernel(ClusterParams c) {
+    __shared__ double m_s[D];
+    const int k = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int L = clamp_len(c.seq_lens[b], c.P * c.T);
+    const int C = kmeans_clusters(c, L);
+    if (k >= C) return;
+    const int i = int((int64_t(k) * L) / C);
+    const KV *row = src_row(c, static_cast<const KV *>(c.k_src), b, g, i);
+    store_centroid<D>(c, b, g, k, double(to_f32(row[threadIdx.x])), m_s);
+}
+
+// 2. Assign (thread per token): the cluster with the largest
+//    k . mu - |mu|^2 / 2, lowest index on ties; -1 past the sequence's end.
+//    The block's keys are staged channel-major in LDS, and the centroids
+//    kCentroidGroup at a time (also channel-major, so one channel's values
+//    for the group are contiguous broadcast reads); the channel loop is a
+//    runtime loop, which keeps the live values to a few channels.
+constexpr int kAssignThreads = 128;
+constexpr int kCentroidGroup = 16;
+
+template <typename KV, int D>
+__global__ __launch_bounds__(kAssignThreads) void kmeans_assign_kernel(ClusterParams c) {
+#pragma clang fp contract(off)
+    constexpr int VPC = KVTraits<KV>::kPerChunk;
+    __shared__ __attribute__((aligned(16))) double mu_s[D][kCentroidGroup];
+    __shared__ double h_s[kCentroidGroup];
+    __shared__ KV k_s[D][kAssignThreads];
+    const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int cap = c.P * c.T;
+    const int L = clamp_len(c.seq_lens[b], cap);
+    const int i = blockIdx.x * kAssignThreads + tid;
+    int32_t *codes = c.codes + (size_t(b) * c.Hkv + g) * size_t(cap);
+    if (blockIdx.x * kAssignThreads >= L) {              // the whole block is past the end
+        if (i < cap) codes[i] = -1;
+        return;
+    }
+    const bool active = i < L;
+    const int C = kmeans_clusters(c, L);
+    if (active) {
+        const KV *row = src_row(c, static_cast<const KV *>(c.k_src), b, g, i);
+#pragma unroll
+        for (int q = 0; q < D / VPC; ++q) {
+            const uint4 v = ld16(row + q * VPC);
+            const KV *ve = reinterpret_cast<const KV *>(&v);
+#pragma unroll
+            for (int u = 0; u < VPC; ++u) k_s[q * VPC + u][tid] = ve[u];
+        }
+    } else {
+        for (int ch = 0; ch < D; ++ch) k_s[ch][tid] = KV(0);
+    }
+    const size_t head = (size_t(b) * c.Hkv + g) * size_t(c.cmax);
+    const double *mu = c.mu + head * D;
+    const double *half = c.half + head;
+    double best = -INFINITY;
+    int bi = 0;
+    for (int c0 = 0; c0 < C; c0 += kCentroidGroup) {
+        const int n = min(kCentroidGroup, C - c0);
+        __syncthreads();                                 // also orders the key staging
+        for (int e = tid; e < kCentroidGroup * D; e += kAssignThreads)
+            mu_s[e % D][e / D] = e / D < n ? mu[size_t(c0) * D + e] : 0.0;
+        if (tid < kCentroidGroup) h_s[tid] = tid < n ? half[c0 + tid] : 0.0;
+        __syncthreads();
+        double dot[kCentroidGroup];
+#pragma unroll
+        for (int u = 0; u < kCentroidGroup; ++u) dot[u] = 0.0;
+#pragma unroll 2
+        for (int ch = 0; ch < D; ++ch) {
+            const double x = double(to_f32(k_s[ch][tid]));
+#pragma unroll
+            for (int u = 0; u < kCentroidGroup; ++u) dot[u] = dot[u] + x * mu_s[ch][u];
+        }
+#pragma unroll
+        for (int u = 0; u < kCentroidGroup; ++u) {
+            if (u < n) {
+                const double score = dot[u] - h_s[u] * 0.5;
+                if (score > best) {
+                    best = score;
+                    bi = c0 + u;
+                }
+            }
+        }
+    }
+    if (i < cap) codes[i] = active ? bi : -1;
+}
+
+// 3. Move (block per cluster, thread per channel): the members are the
+//    cluster's run of the stable sort, so they come in token order.
+template <typename KV, int D>
+__global__ __launch_bounds__(D) void kmeans_update_kernel(ClusterParams c) {
+#pragma clang fp contract(off)
+    __shared__ double m_s[D];
+    const int k = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int cap = c.P * c.T;
+    const int L = clamp_len(c.seq_lens[b], cap);
+    const int C = kmeans_clusters(c, L);
+    if (k >= C) return;
+    const int nb = 1 << c.bits;
+    const int32_t *st = c.starts + (size_t(b) * c.Hkv + g) * size_t(nb + 1);
+    const int s0 = clamp_len(st[k], L), s1 = clamp_len(st[k + 1], L);
+    if (s1 <= s0) return;                                // empty: the centroid stays
+    const int32_t *token_of = c.token_of + (size_t(b) * c.Hkv + g) * size_t(cap);
+    const KV *ks = static_cast<const KV *>(c.k_src);
+    constexpr int kRows = 8;                             // member rows in flight
+    double acc = 0.0;
+    for (int s = s0; s < s1; s += kRows) {
+        float x[kRows];
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+            x[u] = 0.0f;
+            if (s + u < s1) {
+                int t = token_of[s + u];
+                t = t < 0 ? 0 : (t >= L ? L - 1 : t);
+                x[u] = to_f32(src_row(c, ks, b, g, t)[threadIdx.x]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRows; ++u)
+            if (s + u < s1) acc = acc + double(x[u]);
+    }
+    store_centroid<D>(c, b, g, k, acc / double(s1 - s0), m_s);
+}
+
 }  // namespace
 
 santa_status launch_pack_hashed(const ClusterParams &c, void *stream) {
@@ -252,6 +422,38 @@ santa_status launch_pack_hashed(const ClusterParams &c, void *stream) {
         else hipLaunchKernelGGL((pack_hashed_kernel<float, 128>), pgrid, dim3(kBlock), 0, st, c);
     }
     return launched();
+}
+
+namespace {
+
+template <typename KV, int D>
+santa_status run_kmeans(const ClusterParams &c, int32_t iters, hipStream_t st) {
+    const dim3 cgrid(c.cmax, c.Hkv, c.B);
+    const dim3 agrid((c.P * c.T + kAssignThreads - 1) / kAssignThreads, c.Hkv, c.B);
+    hipLaunchKernelGGL((kmeans_init_kernel<KV, D>), cgrid, dim3(D), 0, st, c);
+    santa_status s = launched();
+    for (int it = 0; it < iters && s == SANTA_OK; ++it) {
+        hipLaunchKernelGGL((kmeans_assign_kernel<KV, D>), agrid, dim3(kAssignThreads), 0, st, c);
+        if ((s = launched()) != SANTA_OK) break;
+        hipLaunchKernelGGL(hash_rank_kernel, dim3(c.B * c.Hkv), dim3(kSortThreads), 0, st, c);
+        if ((s = launched()) != SANTA_OK) break;
+        if (it + 1 < iters) {
+            hipLaunchKernelGGL((kmeans_update_kernel<KV, D>), cgrid, dim3(D), 0, st, c);
+            s = launched();
+        }
+    }
+    if (s != SANTA_OK) return s;
+    hipLaunchKernelGGL((pack_hashed_kernel<KV, D>), dim3(c.P, c.Hkv, c.B), dim3(kBlock), 0, st, c);
+    return launched();
+}
+
+}  // namespace
+
+santa_status launch_pack_kmeans(const ClusterParams &c, int32_t iters, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (c.dtype == SANTA_BF16)
+        return c.d == 64 ? run_kmeans<bf16_t, 64>(c, iters, st) : run_kmeans<bf16_t, 128>(c, iters, st);
+    return c.d == 64 ? run_kmeans<float, 64>(c, iters, st) : run_kmeans<float, 128>(c, iters, st);
 }
 
 }  // namespace santa

@@ -366,6 +366,91 @@ santa_status santa_pack_pages_hashed(const santa_kv *kv, const void *k_src, cons
     return launch_pack_hashed(c, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+struct KmeansLayout {
+    int32_t cmax = 0, bits = 0;
+    size_t mu = 0, half = 0, starts = 0, total = 0;
+};
+
+// Clusters allocated per (sequence, KV head) and the workspace sections.
+santa_status kmeans_layout(const santa_kv *kv, int32_t clusters, KmeansLayout *out) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (clusters < 0) return SANTA_ERR_SHAPE;
+    const int64_t cap = int64_t(kv->max_pages_per_seq) * kv->page_size;
+    if (int64_t(kv->batch) * kv->num_kv_heads * cap >= (int64_t(1) << 31)) return SANTA_ERR_SHAPE;
+    const int64_t cmax = clusters > 0 ? std::min<int64_t>(clusters, cap) : kv->max_pages_per_seq;
+    if (cmax > kMaxClusters) return SANTA_ERR_SHAPE;
+    KmeansLayout w;
+    w.cmax = int32_t(std::max<int64_t>(cmax, 1));
+    while ((int64_t(1) << w.bits) < w.cmax) ++w.bits;
+    const size_t heads = size_t(kv->batch) * kv->num_kv_heads;
+    size_t off = 0;
+    w.mu = off;     off = align256(off + heads * w.cmax * size_t(kv->head_dim) * 8);
+    w.half = off;   off = align256(off + heads * w.cmax * 8);
+    w.starts = off; off = align256(off + heads * ((size_t(1) << w.bits) + 1) * 4);
+    w.total = off;
+    *out = w;
+    return SANTA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+santa_status santa_kmeans_workspace_size(const santa_kv *kv, int32_t clusters, size_t *bytes) {
+    if (!bytes) return SANTA_ERR_NULL;
+    KmeansLayout w;
+    const santa_status st = kmeans_layout(kv, clusters, &w);
+    if (st == SANTA_OK) *bytes = w.total;
+    return st;
+}
+
+santa_status santa_pack_pages_kmeans(const santa_kv *kv, const void *k_src, const void *v_src,
+                                     int32_t clusters, int32_t iters, int32_t *codes,
+                                     int32_t *token_of, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    KmeansLayout w;
+    santa_status st = kmeans_layout(kv, clusters, &w);
+    if (st != SANTA_OK) return st;
+    if (!k_src || !v_src || !codes || !token_of) return SANTA_ERR_NULL;
+    if (iters < 1 || iters > kMaxKmeansIters) return SANTA_ERR_SHAPE;
+    if (!workspace || workspace_bytes < w.total || uintptr_t(workspace) % 8 != 0) return SANTA_ERR_WORKSPACE;
+    const uintptr_t bytes = uintptr_t(kv->num_pages) * uintptr_t(kv->num_kv_heads) * uintptr_t(kv->page_size) *
+                            uintptr_t(kv->head_dim) * (kv->dtype == SANTA_BF16 ? 2u : 4u);
+    const uintptr_t lo[4] = {uintptr_t(k_src), uintptr_t(v_src), uintptr_t(kv->k_pages), uintptr_t(kv->v_pages)};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if ((i >= 2 || j >= 2) && lo[i] < lo[j] + bytes && lo[j] < lo[i] + bytes) return SANTA_ERR_SHAPE;
+    char *ws = static_cast<char *>(workspace);
+    ClusterParams c{};
+    c.k_src = k_src;
+    c.v_src = v_src;
+    c.k_dst = const_cast<void *>(kv->k_pages);
+    c.v_dst = const_cast<void *>(kv->v_pages);
+    c.page_table = kv->page_table;
+    c.seq_lens = kv->seq_lens;
+    c.codes = codes;
+    c.token_of = token_of;
+    c.num_pages = kv->num_pages;
+    c.dtype = kv->dtype;
+    c.B = kv->batch;
+    c.Hkv = kv->num_kv_heads;
+    c.P = kv->max_pages_per_seq;
+    c.T = kv->page_size;
+    c.d = kv->head_dim;
+    c.bits = w.bits;
+    c.mu = reinterpret_cast<double *>(ws + w.mu);
+    c.half = reinterpret_cast<double *>(ws + w.half);
+    c.starts = reinterpret_cast<int32_t *>(ws + w.starts);
+    c.clusters = clusters;
+    c.cmax = w.cmax;
+    return launch_pack_kmeans(c, iters, stream);
+}
+
 const char *santa_status_string(int32_t status) {
     switch (status) {
         case SANTA_OK: return "ok";
@@ -378,6 +463,6 @@ const char *santa_status_string(int32_t status) {
     }
 }
 
-int32_t santa_version(void) { return 230; }
+int32_t santa_version(void) { return 240; }
 
 }  // extern "C"

@@ -92,7 +92,16 @@ struct ClusterParams {
     int32_t *token_of;          // [B][Hkv][P * T]
     int64_t num_pages;
     int32_t dtype, B, Hkv, P, T, d, bits;
+    // k-means partition (workspace sections; NULL for the hash partition)
+    double *mu;                 // [B][Hkv][cmax][d] centroids
+    double *half;               // [B][Hkv][cmax] |mu|^2 / 2 terms (the sums, halved at use)
+    int32_t *starts;            // [B][Hkv][2^bits + 1] first sorted position of each code
+    int32_t clusters;           // requested clusters per sequence (0: one per team)
+    int32_t cmax;               // allocated clusters per (sequence, KV head)
 };
+
+constexpr int kMaxClusters = 1 << 10;      // codes must fit the counting sort
+constexpr int kMaxKmeansIters = 1000;
 
 // Host-side argument checks; no HIP calls.
 santa_status validate_kv(const santa_kv *kv);
@@ -105,5 +114,6 @@ santa_status launch_gather(const Params &p, void *stream);
 santa_status launch_combine(const Params &p, void *stream);
 santa_status launch_pack_pages(const PackParams &pp, void *stream);
 santa_status launch_pack_hashed(const ClusterParams &c, void *stream);
+santa_status launch_pack_kmeans(const ClusterParams &c, int32_t iters, void *stream);
 
 }  // namespace santa

@@ -32,6 +32,8 @@ EXPORTED = (
     "santa_attention_given_teams",
     "santa_pack_pages",
     "santa_pack_pages_hashed",
+    "santa_kmeans_workspace_size",
+    "santa_pack_pages_kmeans",
     "santa_status_string",
     "santa_version",
 )
@@ -91,6 +93,8 @@ def load():
         "santa_attention_given_teams": (i32, [kvp, P, i32, P, P, P, P, P, sz, P]),
         "santa_pack_pages": (i32, [i32, ctypes.c_int64, i32, i32, i32, P, P, P, P, P]),
         "santa_pack_pages_hashed": (i32, [kvp, P, P, P, i32, P, P, P]),
+        "santa_kmeans_workspace_size": (i32, [kvp, i32, ctypes.POINTER(sz)]),
+        "santa_pack_pages_kmeans": (i32, [kvp, P, P, i32, i32, P, P, P, sz, P]),
         "santa_status_string": (ctypes.c_char_p, [i32]),
         "santa_version": (i32, []),
     }
@@ -174,26 +178,35 @@ def pack_pages(k_src, v_src, k_dst=None, v_dst=None):
     return k_dst, v_dst
 
 
-def santa_pack_pages_hashed(kv, k_src, v_src, directions, codes=None, token_of=None):
-    """Write kv's pages from plain pages k_src / v_src [num_pages][Hkv][T][d]
-    in hash-partition order for directions [Hkv][bits][d] (float32).
-    Returns (codes, token_of), each [B][Hkv][P*T] int32."""
+def _partition_outputs(kv, k_src, v_src, codes, token_of):
+    """Checks the plain source pages of a re-partitioning pack and returns the
+    (codes, token_of) output tensors, allocated when not given."""
     if k_src.shape != (kv.num_pages, kv.num_kv_heads, kv.page_size, kv.head_dim) or v_src.shape != k_src.shape:
         raise ValueError("k_src and v_src must be [num_pages][Hkv][T][d]")
     if k_src.dtype != kv.dtype or v_src.dtype != kv.dtype or not (k_src.is_contiguous() and v_src.is_contiguous()):
         raise ValueError("k_src and v_src must be contiguous tensors of the cache dtype")
-    if (directions.dtype != torch.float32 or directions.dim() != 3 or not directions.is_contiguous()
-            or directions.shape[0] != kv.num_kv_heads or directions.shape[2] != kv.head_dim):
-        raise ValueError("directions must be a contiguous float32 [Hkv][bits][d] tensor")
+    if k_src.device != kv.device or v_src.device != kv.device:
+        raise ValueError("k_src and v_src must be on the cache's device")
     shape = (kv.batch, kv.num_kv_heads, kv.max_pages_per_seq * kv.page_size)
     _check_tensor("codes", codes, shape, torch.int32, kv.device)
     _check_tensor("token_of", token_of, shape, torch.int32, kv.device)
-    if directions.device != kv.device or k_src.device != kv.device or v_src.device != kv.device:
-        raise ValueError("k_src, v_src and directions must be on the cache's device")
     if codes is None:
         codes = torch.empty(shape, dtype=torch.int32, device=kv.device)
     if token_of is None:
         token_of = torch.empty(shape, dtype=torch.int32, device=kv.device)
+    return codes, token_of
+
+
+def santa_pack_pages_hashed(kv, k_src, v_src, directions, codes=None, token_of=None):
+    """Write kv's pages from plain pages k_src / v_src [num_pages][Hkv][T][d]
+    in hash-partition order for directions [Hkv][bits][d] (float32).
+    Returns (codes, token_of), each [B][Hkv][P*T] int32."""
+    if (directions.dtype != torch.float32 or directions.dim() != 3 or not directions.is_contiguous()
+            or directions.shape[0] != kv.num_kv_heads or directions.shape[2] != kv.head_dim):
+        raise ValueError("directions must be a contiguous float32 [Hkv][bits][d] tensor")
+    if directions.device != kv.device:
+        raise ValueError("directions must be on the cache's device")
+    codes, token_of = _partition_outputs(kv, k_src, v_src, codes, token_of)
     d = kv.desc()
     _check("santa_pack_pages_hashed",
            load().santa_pack_pages_hashed(ctypes.byref(d), _ptr(k_src), _ptr(v_src), _ptr(directions),
@@ -201,17 +214,62 @@ def santa_pack_pages_hashed(kv, k_src, v_src, directions, codes=None, token_of=N
     return codes, token_of
 
 
+def santa_kmeans_workspace_size(kv, clusters=0):
+    """Bytes of workspace santa_pack_pages_kmeans needs for `clusters`."""
+    n = ctypes.c_size_t(0)
+    d = kv.desc()
+    _check("santa_kmeans_workspace_size", load().santa_kmeans_workspace_size(ctypes.byref(d), int(clusters), ctypes.byref(n)))
+    return n.value
+
+
+def santa_pack_pages_kmeans(kv, k_src, v_src, clusters=0, iters=10, codes=None, token_of=None, workspace=None):
+    """Write kv's pages from plain pages k_src / v_src [num_pages][Hkv][T][d]
+    in the order of a k-means partition of each sequence's keys (`clusters`
+    per sequence, 0 for one per team; `iters` assignments). Returns (codes,
+    token_of), each [B][Hkv][P*T] int32; codes are cluster ids."""
+    codes, token_of = _partition_outputs(kv, k_src, v_src, codes, token_of)
+    need = santa_kmeans_workspace_size(kv, clusters)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=kv.device)
+    elif (workspace.device != kv.device or not workspace.is_contiguous()
+          or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on the cache's device")
+    d = kv.desc()
+    _check("santa_pack_pages_kmeans",
+           load().santa_pack_pages_kmeans(ctypes.byref(d), _ptr(k_src), _ptr(v_src), int(clusters), int(iters),
+                                          _ptr(codes), _ptr(token_of), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream()))
+    return codes, token_of
+
+
+def kv_from_workload_kmeans(w, clusters=0, iters=10, device="cuda"):
+    """Upload a workload and pack its pages in k-means order.
+    Returns (KVCache, q tensor, codes, token_of)."""
+    k_src = storage_tensor(w.k_pages, w.dtype, device)
+    v_src = storage_tensor(w.v_pages, w.dtype, device)
+    kv = _empty_cache_like(w, k_src, device)
+    codes, token_of = santa_pack_pages_kmeans(kv, k_src, v_src, clusters, iters)
+    torch.cuda.current_stream().synchronize()
+    del k_src, v_src
+    return kv, storage_tensor(w.q, w.dtype, device), codes, token_of
+
+
+def _empty_cache_like(w, k_src, device):
+    """A zeroed destination cache with the workload's page table and lengths."""
+    n, hkv, T, d = (int(x) for x in k_src.shape)
+    return KVCache(torch.zeros((n, hkv, T * d), dtype=k_src.dtype, device=device),
+                   torch.zeros((n, hkv, T * d), dtype=k_src.dtype, device=device),
+                   torch.from_numpy(np.ascontiguousarray(w.page_table, dtype=np.int32)).to(device),
+                   torch.from_numpy(np.ascontiguousarray(w.seq_lens, dtype=np.int32)).to(device),
+                   w.num_q_heads, w.page_size)
+
+
 def kv_from_workload_hashed(w, directions, device="cuda"):
     """Upload a workload and pack its pages in hash-partition order.
     Returns (KVCache, q tensor, codes, token_of)."""
     k_src = storage_tensor(w.k_pages, w.dtype, device)
     v_src = storage_tensor(w.v_pages, w.dtype, device)
-    n, hkv, T, d = (int(x) for x in k_src.shape)
-    kv = KVCache(torch.zeros((n, hkv, T * d), dtype=k_src.dtype, device=device),
-                 torch.zeros((n, hkv, T * d), dtype=k_src.dtype, device=device),
-                 torch.from_numpy(np.ascontiguousarray(w.page_table, dtype=np.int32)).to(device),
-                 torch.from_numpy(np.ascontiguousarray(w.seq_lens, dtype=np.int32)).to(device),
-                 w.num_q_heads, w.page_size)
+    kv = _empty_cache_like(w, k_src, device)
     dirs = torch.from_numpy(np.ascontiguousarray(directions, dtype=np.float32)).to(device)
     codes, token_of = santa_pack_pages_hashed(kv, k_src, v_src, dirs)
     torch.cuda.current_stream().synchronize()

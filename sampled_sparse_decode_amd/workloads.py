@@ -294,6 +294,15 @@ def permuted_workload(w, k_pages, v_pages, suffix="hashed"):
     return dataclasses.replace(w, name=f"{w.name}_{suffix}", k_pages=k_pages, v_pages=v_pages)
 
 
+def kv_head_slice(w, g):
+    """A copy of workload w reduced to KV head g and its query heads."""
+    G = w.group
+    return dataclasses.replace(w, name=f"{w.name}_kvhead{g}", num_q_heads=G, num_kv_heads=1,
+                               k_pages=np.ascontiguousarray(w.k_pages[:, g:g + 1]),
+                               v_pages=np.ascontiguousarray(w.v_pages[:, g:g + 1]),
+                               q=np.ascontiguousarray(w.q[:, g * G:(g + 1) * G]))
+
+
 FULL_SIZE = {
     "tiny_f32_n1024_m8": lambda: tiny_planted(),
     "qwen7b_32k_b1_m31": lambda: qwen_planted(),

@@ -46,7 +46,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.santa_version() == 230
+    assert lib.santa_version() == 240
     for code in range(6):
         assert S.santa_status_string(code)
     assert S.santa_status_string(99) == "unknown status"
@@ -204,6 +204,48 @@ def test_pack_pages_hashed_validation(lib):
     assert call(ctypes.byref(k), F, far2, F, 4, F, F, None) == SHAPE          # source overlaps destination
     assert call(ctypes.byref(kv()), far, far2, F, 4, F, F, None) == SHAPE     # destinations overlap
     assert call(ctypes.byref(kv(head_dim=80)), far, far2, F, 4, F, F, None) == UNSUP
+
+
+def test_kmeans_workspace_size(lib):
+    """Centroids [B][Hkv][cmax][d] float64, |mu|^2 [B][Hkv][cmax] float64 and
+    the sort offsets [B][Hkv][2^bits + 1] int32, each section 256-aligned."""
+    n = ctypes.c_size_t(0)
+    size = lib.santa_kmeans_workspace_size
+    a = lambda x: (x + 255) // 256 * 256
+    B, Hkv, P, d = 2, 4, 256, 128
+    assert size(ctypes.byref(kv()), 0, ctypes.byref(n)) == OK              # one cluster per team: cmax = P
+    assert n.value == a(B * Hkv * P * d * 8) + a(B * Hkv * P * 8) + a(B * Hkv * (256 + 1) * 4)
+    assert size(ctypes.byref(kv()), 100, ctypes.byref(n)) == OK            # bits = 7
+    assert n.value == a(B * Hkv * 100 * d * 8) + a(B * Hkv * 100 * 8) + a(B * Hkv * (128 + 1) * 4)
+    assert size(ctypes.byref(kv(max_pages_per_seq=2, num_pages=4)), 1000, ctypes.byref(n)) == OK   # capped at P*T
+    assert n.value == a(B * Hkv * 256 * d * 8) + a(B * Hkv * 256 * 8) + a(B * Hkv * (256 + 1) * 4)
+    assert size(ctypes.byref(kv()), 1025, ctypes.byref(n)) == SHAPE
+    assert size(ctypes.byref(kv(max_pages_per_seq=1025, num_pages=4096)), 0, ctypes.byref(n)) == SHAPE
+    assert size(ctypes.byref(kv()), -1, ctypes.byref(n)) == SHAPE
+    assert size(ctypes.byref(kv()), 0, None) == NULL
+
+
+def test_pack_pages_kmeans_validation(lib):
+    """santa_pack_pages_kmeans checks its arguments on the host."""
+    k = kv(v_pages=FAKE + (3 << 40))
+    call = lib.santa_pack_pages_kmeans
+    far = ctypes.c_void_p(FAKE + (1 << 40))
+    far2 = ctypes.c_void_p(FAKE + (2 << 40))
+    F = ctypes.c_void_p(FAKE)
+    big = 1 << 40
+    assert call(ctypes.byref(k), None, far2, 0, 5, F, F, F, big, None) == NULL
+    assert call(ctypes.byref(k), far, far2, 0, 5, None, F, F, big, None) == NULL
+    assert call(ctypes.byref(k), far, far2, 0, 5, F, None, F, big, None) == NULL
+    assert call(ctypes.byref(k), far, far2, 0, 0, F, F, F, big, None) == SHAPE          # iters
+    assert call(ctypes.byref(k), far, far2, 0, 1001, F, F, F, big, None) == SHAPE
+    assert call(ctypes.byref(k), far, far2, 1025, 5, F, F, F, big, None) == SHAPE       # clusters
+    assert call(ctypes.byref(k), far, far2, -3, 5, F, F, F, big, None) == SHAPE
+    assert call(ctypes.byref(k), far, far2, 0, 5, F, F, None, big, None) == WS
+    assert call(ctypes.byref(k), far, far2, 0, 5, F, F, F, 1024, None) == WS
+    assert call(ctypes.byref(k), far, far2, 0, 5, F, F, ctypes.c_void_p(FAKE + 4), big, None) == WS   # alignment
+    assert call(ctypes.byref(k), F, far2, 0, 5, F, F, F, big, None) == SHAPE            # source overlaps destination
+    assert call(ctypes.byref(kv()), far, far2, 0, 5, F, F, F, big, None) == SHAPE       # destinations overlap
+    assert call(ctypes.byref(kv(head_dim=80)), far, far2, 0, 5, F, F, F, big, None) == UNSUP
 
 
 def test_binding_rejects_mismatched_buffers():
