@@ -206,6 +206,24 @@ def test_pack_pages_hashed_validation(lib):
     assert call(ctypes.byref(kv(head_dim=80)), far, far2, F, 4, F, F, None) == UNSUP
 
 
+def test_plain_c_consumer(lib, tmp_path):
+    """tests/c_consumer.c, built with gcc as C99 against include/santa.h and
+    linked with libsanta.so, runs its host-only checks."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = tmp_path / "c_consumer"
+    libdir = os.path.dirname(S.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_consumer.c"),
+                    "-o", str(exe), f"-L{libdir}", "-lsanta", f"-Wl,-rpath,{libdir}"], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert "c consumer ok" in res.stdout
+
+
 def test_kmeans_workspace_size(lib):
     """Centroids [B][Hkv][cmax][d] float64, |mu|^2 [B][Hkv][cmax] float64 and
     the sort offsets [B][Hkv][2^bits + 1] int32, each section 256-aligned."""
