@@ -131,7 +131,7 @@ __device__ int load_team_list(const Params &p, TeamList &tl, int s, int g, int b
 // pair: a head with no team in the block gets an empty one (max -inf), which
 // the combine skips.
 __device__ __forceinline__ void write_empty_partial(const Params &p, int head, int s) {
-    reinterpret_cast<float2 *>(p.part_ml)[size_t(head) * p.P + s] = make_float2(kNegInfF, 0.0f);
+    reinterpret_cast<float2 *>(p.part_ml)[size_t(head) * p.slots + s] = make_float2(kNegInfF, 0.0f);
 }
 
 // Union-rank team list (multi-team SANTA++ blocks): block s takes the teams
@@ -393,7 +393,7 @@ __device__ __forceinline__ void mfma_store_partial(const Params &p, MfmaReduce<D
     float2 *part_ml = reinterpret_cast<float2 *>(p.part_ml);
     for (int idx = tid; idx < G * D; idx += kBlock) {
         const int h = idx / D, c = idx - h * D;
-        const size_t slot = size_t(hbase + h) * p.P + s;
+        const size_t slot = size_t(hbase + h) * p.slots + s;
         if (rd.hm[h] == kNegInfF) {                 // no team of this block for the head
             if (p.ranked && c == 0) write_empty_partial(p, hbase + h, s);
             continue;
@@ -446,7 +446,7 @@ struct GroupChunks {
 };
 
 // Round trip 1 and the union: words, popcount prefix; returns the union size.
-__device__ int group_union(const Params &p, GroupChunks &gc, int g, int b) {
+__device__ __forceinline__ void group_load(const Params &p, GroupChunks &gc, int g, int b) {
     const int tid = threadIdx.x;
     const int G = p.G;
     const bool dense = p.mode == kModeDense;
@@ -460,6 +460,14 @@ __device__ int group_union(const Params &p, GroupChunks &gc, int g, int b) {
         }
     if (tid == 0) gc.len = clamp_len(Lraw, p.P * p.T);
     __syncthreads();
+}
+
+// The union words and their popcount prefix from the loaded group data;
+// returns the union size.
+__device__ __forceinline__ int group_scan(const Params &p, GroupChunks &gc) {
+    const int tid = threadIdx.x;
+    const int G = p.G;
+    const bool dense = p.mode == kModeDense;
     if (tid < 64) {
         const int K = (gc.len + p.T - 1) / p.T;
         uint32_t u = 0u;
@@ -485,6 +493,11 @@ __device__ int group_union(const Params &p, GroupChunks &gc, int g, int b) {
     }
     __syncthreads();
     return gc.upre[p.words];
+}
+
+__device__ int group_union(const Params &p, GroupChunks &gc, int g, int b) {
+    group_load(p, gc, g, b);
+    return group_scan(p, gc);
 }
 
 // Chunks c0 .. c0 + cnt - 1 (cnt <= kWin) of the group: team, heads, page,
@@ -563,6 +576,165 @@ __global__ __launch_bounds__(kBlock, 3) void gather_balanced_kernel(Params p) {
         __syncthreads();                          // the window is reused
     }
     mfma_store_partial<D>(p, lds.rd, m, lsum, o, hbase, j);
+}
+
+// ---------------------------------------------------------------------------
+// Dense gather for batch >= 2 (bf16), with a plan chosen per launch from the
+// sequence lengths (round trip 1, beside the per-group plan's own metadata).
+//   Even lengths: the per-group plan of gather_balanced_kernel — block j
+//     takes range j mod nb of the nb = max_splits even ranges of group
+//     j / nb — whose metadata round trip is the first one, so it costs
+//     nothing extra.
+//   Ragged lengths (some group above 5/4 of the mean number of teams): one
+//     even split of the chunks of all groups, in group order, over the grid,
+//     so that long sequences do not finish last on a few blocks. A block
+//     walks the groups its range [j C / nbe, (j + 1) C / nbe) overlaps
+//     (usually one or two), each with a metadata round trip, the chunk loop
+//     and a partial store; group X's partial from block j goes to slot
+//     j - J(X), J(X) the block holding X's first chunk.
+// Block 0 writes every group's slot count for the combine. (SANTA++ keeps
+// the per-group plan: its union sizes are even enough that one split over
+// all groups measured slower, its extra round trips outweighing the balance.)
+// ---------------------------------------------------------------------------
+constexpr int kRaggedNum = 5, kRaggedDen = 4;   // ragged: largest group > 5/4 of the mean
+
+// The block whose range holds chunk c (ranges [j C / nbe, (j + 1) C / nbe)).
+__device__ __forceinline__ int spread_block_of(int c, int total, int nbe) {
+    return int(((int64_t(c) + 1) * nbe - 1) / total);
+}
+
+template <int D>
+union DenseLds {
+    struct {
+        GroupChunks gc;
+        __attribute__((aligned(16))) bf16_t q_lds[kGM][D + 8];
+    } st;
+    MfmaReduce<D> rd;                             // used by each partial store
+};
+
+// Chunks [lo, hi) of the group whose metadata is in lds (dense: every head
+// takes every chunk with weight 1), merged into one partial at slot s.
+template <int D>
+__device__ __forceinline__ void dense_stream_range(const Params &p, DenseLds<D> &lds, int g, int hbase, int lo,
+                                                   int hi, int s) {
+    constexpr int NT = D / 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int cpt = p.T >= 32 ? p.T / 32 : 1;
+    GroupChunks &gc = lds.st.gc;
+    float m = kNegInfF, lsum = 0.0f;
+    f32x4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w0 = lo; w0 < hi; w0 += kWin) {
+        const int cnt = min(kWin, hi - w0);
+        chunk_window(p, gc, cpt, w0, cnt);
+        for (int q = wave; q < cnt; q += kWaves) {
+            const bool drew = (gc.mask[q] >> i16) & 1u;
+            MfmaChunk<D> ck;
+            mfma_load_chunk_at<D>(p, gc.page[q], gc.n[q], gc.tb[q], g, i16, g4, ck);
+            mfma_compute_chunk_at<D>(p, gc.n[q], gc.tb[q], drew ? 0.0f : kNegInfF, i16, g4, lds.st.q_lds, ck, m,
+                                     lsum, o);
+        }
+        __syncthreads();                          // the window is reused
+    }
+    mfma_store_partial<D>(p, lds.rd, m, lsum, o, hbase, s);
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock, 3) void gather_dense_spread_kernel(Params p) {
+    __shared__ DenseLds<D> lds;
+    __shared__ int32_t ucnt[kMaxSpreadGroups];          // teams of each group
+    __shared__ int32_t ustart[kMaxSpreadGroups + 1];    // first chunk of each group; [ngroups] = all chunks
+    __shared__ int32_t ragged_s;
+    GroupChunks &gc = lds.st.gc;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ngroups = p.B * p.Hkv;
+    const int cpt = p.T >= 32 ? p.T / 32 : 1;
+    const int j = blockIdx.x, nb = p.max_splits;
+    const int xe = min(j / nb, ngroups - 1);             // the block's group in the per-group plan
+    const int be = xe / p.Hkv, ge = xe - be * p.Hkv;
+
+    // Round trip 1: every group's team count, and the per-group plan's
+    // query rows, page-table row and length.
+    for (int x = tid; x < ngroups; x += kBlock) {
+        const int L = clamp_len(p.seq_lens[x / p.Hkv], p.P * p.T);
+        ucnt[x] = (L + p.T - 1) / p.T;
+    }
+    fill_q_lds<D>(p, lds.st.q_lds, be * p.Hq + ge * p.G);
+    group_load(p, gc, ge, be);                           // ends with a barrier
+    if (wave == 0) {
+        // Exclusive prefix of chunk counts (four consecutive groups per lane)
+        // and the largest group.
+        constexpr int PER = kMaxSpreadGroups / 64;
+        int v[PER], sum = 0, mx = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int x = lane * PER + k;
+            v[k] = x < ngroups ? ucnt[x] * cpt : 0;
+            sum += v[k];
+            mx = max(mx, v[k]);
+        }
+        int incl = sum;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+        int run = incl - sum;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int x = lane * PER + k;
+            if (x < ngroups) ustart[x] = run;
+            run += v[k];
+        }
+        if (lane == 63) {
+            ustart[ngroups] = incl;
+            ragged_s = int64_t(mx) * ngroups * kRaggedDen > int64_t(incl) * kRaggedNum;
+        }
+    }
+    __syncthreads();
+    const int total = ustart[ngroups];
+    const bool ragged = ragged_s != 0;
+    const int nbe = min(min(int(gridDim.x), p.slots), total);   // a group's slots stay below p.slots
+    if (j == 0)
+        for (int x = tid; x < ngroups; x += kBlock)
+            p.grp_slots[x] = !ragged ? nb
+                             : ucnt[x] == 0 ? 0
+                                            : spread_block_of(ustart[x + 1] - 1, total, nbe) -
+                                                  spread_block_of(ustart[x], total, nbe) + 1;
+
+    if (!ragged) {
+        if (j / nb >= ngroups) return;                   // no such block in the per-group grid
+        const int U = group_scan(p, gc);
+        const int jl = j - xe * nb, all = U * cpt;
+        dense_stream_range<D>(p, lds, ge, be * p.Hq + ge * p.G, int(int64_t(all) * jl / nb),
+                              int(int64_t(all) * (jl + 1) / nb), jl);
+        return;
+    }
+    if (j >= nbe) return;
+    const int c0 = int(int64_t(total) * j / nbe), c1 = int(int64_t(total) * (j + 1) / nbe);
+    int x = 0;                                           // the last group starting at or before c0
+    {
+        int lo = 0, hi = ngroups - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (ustart[mid] <= c0) lo = mid; else hi = mid - 1;
+        }
+        x = lo;
+    }
+    for (; x < ngroups && ustart[x] < c1; ++x) {
+        if (ustart[x + 1] == ustart[x]) continue;          // no chunk in this group
+        const int b = x / p.Hkv, g = x - b * p.Hkv;
+        const int hbase = b * p.Hq + g * p.G;
+        __syncthreads();                                     // LDS is free again (previous store, plan reads)
+        fill_q_lds<D>(p, lds.st.q_lds, hbase);
+        const int U = group_union(p, gc, g, b);
+        const int lo = max(c0, ustart[x]) - ustart[x];
+        const int hi = min(min(c1, ustart[x + 1]) - ustart[x], U * cpt);
+        dense_stream_range<D>(p, lds, g, hbase, lo, hi, j - spread_block_of(ustart[x], total, nbe));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -669,7 +841,7 @@ __global__ __launch_bounds__(kBlock) void gather_f32_kernel(Params p) {
     float2 *part_ml = reinterpret_cast<float2 *>(p.part_ml);
     for (int idx = tid; idx < G * D; idx += kBlock) {
         const int h = idx / D, cc = idx - h * D;
-        const size_t slot = size_t(hbase + h) * p.P + s;
+        const size_t slot = size_t(hbase + h) * p.slots + s;
         if (m_s[h] == -INFINITY) {             // the head drew no team of this split
             if (p.ranked && cc == 0) write_empty_partial(p, hbase + h, s);
             continue;
@@ -713,9 +885,12 @@ __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
     const int bh = blockIdx.x;
     const int b = bh / p.Hq;
     const bool dense = p.mode == kModeDense;
-    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + size_t(bh) * p.P;
-    const float4 *pacc = reinterpret_cast<const float4 *>(p.part_acc + size_t(bh) * p.P * D);
+    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + size_t(bh) * p.slots;
+    const float4 *pacc = reinterpret_cast<const float4 *>(p.part_acc + size_t(bh) * p.slots * D);
     const int c4 = tid % Q4, sb = tid / Q4;
+    // Slots of this head's group: written by the spread gather, else every
+    // slot below max_splits.
+    const int nsp = p.spread ? p.grp_slots[b * p.Hkv + (bh - b * p.Hq) / p.G] : p.max_splits;
 
     if (p.max_splits <= kFew * SUB) {
         // Few slots (every balanced split at batch >= 1 up to 64 / 128 slots):
@@ -733,84 +908,86 @@ __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
             x[u] = (sp < p.max_splits) ? pacc[size_t(sp) * Q4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         __syncthreads();
-        if (wave == 0) {
-            const int L = clamp_len(Lraw, p.P * p.T);
-            const int K = (L + p.T - 1) / p.T;
-            const int nslots = (K + p.tps - 1) / p.tps;
-            const uint32_t low = (p.tps >= 32) ? 0xffffffffu : ((1u << p.tps) - 1u);
-            float mv[2];
-            bool ok[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int sp = lane + 64 * i;
-                bool hv = sp < p.max_splits;
-                if (hv) {
-                    if (p.ranked) {
-                        hv = ml_s[sp].x != kNegInfF;
-                    } else {
-                        hv = sp < nslots;
-                        if (hv && !dense) {
-                            const int t0 = sp * p.tps;
-                            hv = ((hw_s[t0 >> 5] >> (t0 & 31)) & low) != 0u;
+        if (nsp <= p.max_splits) {                // uniform; else the slot count needs the general path
+            if (wave == 0) {
+                const int L = clamp_len(Lraw, p.P * p.T);
+                const int K = (L + p.T - 1) / p.T;
+                const int nslots = (K + p.tps - 1) / p.tps;
+                const uint32_t low = (p.tps >= 32) ? 0xffffffffu : ((1u << p.tps) - 1u);
+                float mv[2];
+                bool ok[2];
+    #pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int sp = lane + 64 * i;
+                    bool hv = sp < nsp;
+                    if (hv) {
+                        if (p.ranked) {
+                            hv = ml_s[sp].x != kNegInfF;
+                        } else {
+                            hv = sp < nslots;
+                            if (hv && !dense) {
+                                const int t0 = sp * p.tps;
+                                hv = ((hw_s[t0 >> 5] >> (t0 & 31)) & low) != 0u;
+                            }
                         }
                     }
+                    ok[i] = hv;
+                    mv[i] = hv ? ml_s[sp].x : kNegInfF;
                 }
-                ok[i] = hv;
-                mv[i] = hv ? ml_s[sp].x : kNegInfF;
+                float mstar = fmaxf(mv[0], mv[1]);
+                for (int off = 32; off > 0; off >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, off, 64));
+                float lpart = 0.0f;
+    #pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int sp = lane + 64 * i;
+                    const float f = ok[i] ? expf(mv[i] - mstar) : 0.0f;
+                    if (sp < kFew * SUB) f_s[sp] = f;
+                    if (ok[i]) lpart += f * ml_s[sp].y;
+                }
+                for (int off = 32; off > 0; off >>= 1) lpart += __shfl_xor(lpart, off, 64);
+                if (lane == 0) {
+                    redf[0] = mstar;
+                    redf[1] = lpart;
+                }
             }
-            float mstar = fmaxf(mv[0], mv[1]);
-            for (int off = 32; off > 0; off >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, off, 64));
-            float lpart = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int sp = lane + 64 * i;
-                const float f = ok[i] ? expf(mv[i] - mstar) : 0.0f;
-                if (sp < kFew * SUB) f_s[sp] = f;
-                if (ok[i]) lpart += f * ml_s[sp].y;
+            __syncthreads();
+            const float mstar = redf[0], l = redf[1];
+            if (mstar == kNegInfF) {                  // no partial: empty sequence
+                for (int c = tid; c < D; c += kCombine) p.out[size_t(bh) * D + c] = 0.0f;
+                if (tid == 0 && p.lse) p.lse[bh] = kNegInfF;
+                return;
             }
-            for (int off = 32; off > 0; off >>= 1) lpart += __shfl_xor(lpart, off, 64);
-            if (lane == 0) {
-                redf[0] = mstar;
-                redf[1] = lpart;
+            float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    #pragma unroll
+            for (int u = 0; u < kFew; ++u) {
+                const int sp = sb + u * SUB;
+                const float f = (sp < p.max_splits) ? f_s[sp] : 0.0f;
+                if (f > 0.0f) {
+                    a.x += f * x[u].x; a.y += f * x[u].y; a.z += f * x[u].z; a.w += f * x[u].w;
+                }
             }
-        }
-        __syncthreads();
-        const float mstar = redf[0], l = redf[1];
-        if (mstar == kNegInfF) {                  // no partial: empty sequence
-            for (int c = tid; c < D; c += kCombine) p.out[size_t(bh) * D + c] = 0.0f;
-            if (tid == 0 && p.lse) p.lse[bh] = kNegInfF;
+            acc_s[sb][c4] = a;
+            __syncthreads();
+            if (tid < Q4) {
+                float4 sum = acc_s[0][tid];
+                for (int i = 1; i < SUB; ++i) {
+                    const float4 y = acc_s[i][tid];
+                    sum.x += y.x; sum.y += y.y; sum.z += y.z; sum.w += y.w;
+                }
+                const float inv = 1.0f / l;
+                reinterpret_cast<float4 *>(p.out + size_t(bh) * D)[tid] =
+                    make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+                if (tid == 0 && p.lse) p.lse[bh] = mstar + logf(l);
+            }
             return;
         }
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < kFew; ++u) {
-            const int sp = sb + u * SUB;
-            const float f = (sp < p.max_splits) ? f_s[sp] : 0.0f;
-            if (f > 0.0f) {
-                a.x += f * x[u].x; a.y += f * x[u].y; a.z += f * x[u].z; a.w += f * x[u].w;
-            }
-        }
-        acc_s[sb][c4] = a;
-        __syncthreads();
-        if (tid < Q4) {
-            float4 sum = acc_s[0][tid];
-            for (int i = 1; i < SUB; ++i) {
-                const float4 y = acc_s[i][tid];
-                sum.x += y.x; sum.y += y.y; sum.z += y.z; sum.w += y.w;
-            }
-            const float inv = 1.0f / l;
-            reinterpret_cast<float4 *>(p.out + size_t(bh) * D)[tid] =
-                make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
-            if (tid == 0 && p.lse) p.lse[bh] = mstar + logf(l);
-        }
-        return;
     }
 
     // Round trip 1. Slot (max, sum) values are read for every slot that can
     // exist (all inside the workspace); stale ones are ignored below.
     const int Lraw = p.seq_lens[b];
     if (!dense && !p.ranked && tid < p.words) hw_s[tid] = p.bitmaps[size_t(bh) * p.words + tid];
-    const int nslots_max = p.max_splits;
+    const int nslots_max = p.spread ? nsp : p.max_splits;
     float2 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -920,7 +1097,11 @@ __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
 santa_status launch_gather(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(p.max_splits, p.Hkv, p.B);
-    if (p.dtype == SANTA_BF16 && p.balanced) {
+    if (p.dtype == SANTA_BF16 && p.balanced && p.spread && p.mode == kModeDense) {
+        const dim3 sgrid(p.max_splits * p.Hkv * p.B);
+        if (p.d == 64) hipLaunchKernelGGL((gather_dense_spread_kernel<64>), sgrid, dim3(kBlock), 0, st, p);
+        else hipLaunchKernelGGL((gather_dense_spread_kernel<128>), sgrid, dim3(kBlock), 0, st, p);
+    } else if (p.dtype == SANTA_BF16 && p.balanced) {
         if (p.mode == kModeDense) {
             if (p.d == 64) hipLaunchKernelGGL((gather_balanced_kernel<64, kModeDense>), grid, dim3(kBlock), 0, st, p);
             else hipLaunchKernelGGL((gather_balanced_kernel<128, kModeDense>), grid, dim3(kBlock), 0, st, p);

@@ -34,11 +34,14 @@ WorkspaceLayout workspace_layout(const santa_kv &kv) {
     const size_t B = kv.batch, Hq = kv.num_q_heads, P = kv.max_pages_per_seq, d = kv.head_dim;
     w.words = (kv.max_pages_per_seq + 31) / 32;
     w.max_splits = kv.max_pages_per_seq;
+    w.slots = kv.dtype == SANTA_BF16 ? std::max<int32_t>(kv.max_pages_per_seq, kSpreadBlocks) : kv.max_pages_per_seq;
+    const size_t S = size_t(w.slots);
     size_t off = 0;
-    w.bitmaps = off;  off = align256(off + B * Hq * size_t(w.words) * 4);
-    w.lnw = off;      off = align256(off + B * Hq * P * 4);
-    w.part_ml = off;  off = align256(off + B * Hq * P * 8);
-    w.part_acc = off; off = align256(off + B * Hq * P * d * 4);
+    w.bitmaps = off;   off = align256(off + B * Hq * size_t(w.words) * 4);
+    w.lnw = off;       off = align256(off + B * Hq * P * 4);
+    w.part_ml = off;   off = align256(off + B * Hq * S * 8);
+    w.part_acc = off;  off = align256(off + B * Hq * S * d * 4);
+    w.grp_slots = off; off = align256(off + size_t(kv.batch) * kv.num_kv_heads * 4);
     w.total = off;
     return w;
 }
@@ -67,6 +70,7 @@ static void balanced_split(Params *p) {
     p->balanced = 1;
     p->ranked = 1;
     p->tps = 1;
+    p->spread = 0;
     p->max_splits = int32_t(std::min<int64_t>(p->P, std::max<int64_t>(1, (kBalancedBlocks + groups - 1) / groups)));
 }
 
@@ -108,6 +112,7 @@ static Params base_params(const santa_kv &kv, const void *q, float *out, float *
     p.T = kv.page_size;
     p.P = kv.max_pages_per_seq;
     p.words = w.words;
+    p.slots = w.slots;
     p.scale = 1.0 / std::sqrt(double(kv.head_dim));
     char *ws = static_cast<char *>(workspace);
     if (ws) {
@@ -115,6 +120,7 @@ static Params base_params(const santa_kv &kv, const void *q, float *out, float *
         p.lnw = reinterpret_cast<float *>(ws + w.lnw);
         p.part_ml = reinterpret_cast<float *>(ws + w.part_ml);
         p.part_acc = reinterpret_cast<float *>(ws + w.part_acc);
+        p.grp_slots = reinterpret_cast<int32_t *>(ws + w.grp_slots);
     }
     p.out = out;
     p.lse = lse;
@@ -283,6 +289,9 @@ santa_status dense_decode_attention(const santa_kv *kv, const void *q, float *ou
     p.mode = kModeDense;
     if (p.dtype == SANTA_BF16) {
         balanced_split(&p);
+        // Batch >= 2: the kernel picks a split over all groups when the
+        // lengths are ragged (they are known only on the device).
+        if (p.B >= 2 && int64_t(p.B) * p.Hkv <= kMaxSpreadGroups) p.spread = 1;
     } else {
         p.tps = teams_per_split(int64_t(p.B) * p.Hkv * p.P, 512);
         while (p.tps < kMaxTeamsPerSplit && (p.P + p.tps - 1) / p.tps > 128) p.tps *= 2;

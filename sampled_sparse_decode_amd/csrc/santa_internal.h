@@ -21,12 +21,20 @@ enum Mode : int32_t { kModeSanta = 0, kModeDense = 1 };
 struct WorkspaceLayout {
     size_t bitmaps;     // uint32 [B][Hq][words]      team bitmap of each query head
     size_t lnw;         // float  [B][Hq][P]          log weight of each drawn team
-    size_t part_ml;     // float2 [B][Hq][P]          split partial (max, sum)
-    size_t part_acc;    // float  [B][Hq][P][d]       split partial weighted value sums
+    size_t part_ml;     // float2 [B][Hq][slots]      split partial (max, sum)
+    size_t part_acc;    // float  [B][Hq][slots][d]   split partial weighted value sums
+    size_t grp_slots;   // int32  [B][Hkv]            partial slots of each group (spread gather)
     size_t total;
     int32_t words;      // ceil(P / 32)
     int32_t max_splits; // P
+    int32_t slots;      // partial slots per head: P (float32), max(P, kSpreadBlocks) (bfloat16)
 };
+
+// Dense gather of a ragged batch (bfloat16, batch >= 2): one even split of all
+// groups' chunks over the grid, at most max(P, kSpreadBlocks) blocks meeting a
+// group; used while the groups fit its plan.
+constexpr int kSpreadBlocks = 256;
+constexpr int kMaxSpreadGroups = 256;
 
 WorkspaceLayout workspace_layout(const santa_kv &kv);
 
@@ -48,6 +56,9 @@ struct Params {
     int32_t max_splits;     // gather grid.x
     int32_t ranked;         // 1: every split slot < max_splits gets a (max, sum) pair, -inf if empty
     int32_t balanced;       // 1 (bf16 only): block j takes the j-th of max_splits even ranges of union chunks
+    int32_t spread;         // 1 (bf16 dense, batch >= 2): per-launch plan, per group or over all groups
+    int32_t slots;          // partial slots per head (stride of part_ml / part_acc)
+    int32_t *grp_slots;     // spread: [B][Hkv] partial slots written for each group
     double scale;           // 1 / sqrt(d)
     uint32_t *bitmaps;
     float *lnw;

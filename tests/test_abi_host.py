@@ -14,6 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "santa.h")
 
 OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+S_F32 = 0
 FAKE = 0x10000      # non-NULL pointer value; never dereferenced by validation
 
 
@@ -61,8 +62,16 @@ def test_workspace_size_layout(lib):
     def a(x):
         return (x + 255) // 256 * 256
     words = (P + 31) // 32
-    expect = a(B * Hq * words * 4) + a(B * Hq * P * 4) + a(B * Hq * P * 8) + a(B * Hq * P * d * 4)
+    S = max(P, 256)                      # partial slots per head of a bfloat16 cache
+    expect = a(B * Hq * words * 4) + a(B * Hq * P * 4) + a(B * Hq * S * 8) + a(B * Hq * S * d * 4) + a(B * 4 * 4)
     assert n.value == expect
+    # Few pages: the spread gather's 256 slots per head; float32 keeps P.
+    k = kv(max_pages_per_seq=8)
+    assert lib.santa_workspace_size(ctypes.byref(k), 31, ctypes.byref(n)) == OK
+    assert n.value == a(B * Hq * 4) + a(B * Hq * 8 * 4) + a(B * Hq * 256 * 8) + a(B * Hq * 256 * d * 4) + a(B * 4 * 4)
+    k = kv(max_pages_per_seq=8, dtype=S_F32)
+    assert lib.santa_workspace_size(ctypes.byref(k), 31, ctypes.byref(n)) == OK
+    assert n.value == a(B * Hq * 4) + a(B * Hq * 8 * 4) + a(B * Hq * 8 * 8) + a(B * Hq * 8 * d * 4) + a(B * 4 * 4)
 
 
 @pytest.mark.parametrize("over,code", [

@@ -29,6 +29,11 @@ def say(*a):
     print(*a, flush=True)
 
 
+def _with_lens(w, lens):
+    """Workload w with its sequence lengths replaced (each at most its capacity)."""
+    return W.dataclasses.replace(w, seq_lens=np.asarray(lens, dtype=w.seq_lens.dtype))
+
+
 SMALL = {
     "tiny_f32": lambda: W.tiny_planted(),
     "qwen_bf16_ragged": lambda: W.qwen_planted(batch=1, seq_len=4096 + 77, M=31),
@@ -51,6 +56,16 @@ SMALL = {
     # the longest page table (2048 teams of 16 tokens), 16-head groups
     "bf16_b3_g16_p2048": lambda: W.qwen_planted(batch=3, seq_len=32768, T=16, M=24, hq=48, hkv=3,
                                                             d=64, plants=2),
+    # ragged batches: dense decode then splits all groups' chunks evenly over
+    # the grid — a dominant group whose slot count exceeds the combine's
+    # first read, empty groups, and 256 small groups whose blocks each span
+    # several groups
+    "bf16_b2_hkv1_skewed": lambda: _with_lens(W.qwen_planted(batch=2, seq_len=12000, T=32, M=20, hq=4, hkv=1,
+                                                             d=64, plants=3), [150, 12000]),
+    "bf16_b4_empty_groups": lambda: _with_lens(W.qwen_mixed_query(batch=4, seq_len=9000, T=64, M=24, hq=8,
+                                                                  hkv=2, d=128), [0, 3000, 50, 9000]),
+    "bf16_b64_256_groups": lambda: W.paged_ragged(num_seqs=64, len_min=1, len_max=400, T=16, M=6, hq=8, hkv=4,
+                                                  d=64),
     # a full 16-head group over 300 small teams
     "bf16_g16_p300": lambda: W.qwen_planted(batch=1, seq_len=4800, T=16, M=40, hq=16, hkv=1, d=64,
                                                         plants=3),
@@ -217,6 +232,20 @@ def test_edge_cases_empty_short_full_and_single_draw():
     for b in range(w.batch):
         for h in range(w.num_q_heads):
             parity.check_dense_head(w, okv, b, h, dout[b, h], dlse[b, h])
+
+
+def test_all_sequences_empty():
+    # Every group empty: the split has no chunk at all; outputs are zeros
+    # with log-sum-exp -inf for both paths.
+    w = _with_lens(W.paged_ragged(num_seqs=3, len_min=100, len_max=900, T=32, M=5, hq=4, hkv=2, d=64), [0, 0, 0])
+    say("[edge] all sequences empty, B=3")
+    kv, q = S.kv_from_workload(w)
+    reps = S.santa_build_reps(kv)
+    out, lse, teams, _ = run_santa(w, kv, q, reps)
+    dout, dlse = S.dense_decode_attention(kv, q)
+    torch.cuda.synchronize()
+    assert np.all(out == 0) and np.all(np.isneginf(lse)) and np.all(teams == -1)
+    assert torch.all(dout == 0) and torch.all(torch.isneginf(dlse))
 
 
 FULL = {
