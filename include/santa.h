@@ -61,8 +61,9 @@
  * A team is one page: team t of sequence b is tokens [t*T, min((t+1)*T, L_b))
  * stored in physical page page_table[b][t] (T = page_size). The pages leave
  * the team partition open ([EXP] 3.2); contiguous runs, one per page, are
- * the default, and santa_pack_pages_hashed writes each sequence's tokens in
- * a hash-partition order so that the same pages hold clustered teams.
+ * the default; santa_pack_pages_hashed and santa_pack_pages_kmeans write
+ * each sequence's tokens in a hash- or k-means-partition order so that the
+ * same pages hold clustered teams.
  * Sequence b has K_b = ceil(L_b / T) teams.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  */
@@ -113,9 +114,10 @@ typedef struct santa_kv {
 /* Bytes of device workspace that santa_decode_attention,
  * santa_attention_given_teams and dense_decode_attention need for this cache
  * shape. The workspace holds per-head team bitmaps and weights and the
- * split-K partial results; its contents need no initialisation and are
- * meaningless after the call. Returns SANTA_OK and writes *bytes, or a
- * validation status. */
+ * split-K partial results; its contents need no initialisation. After
+ * santa_select_teams(_ex) it holds the drawn sets that santa_attend_selected
+ * reads; after any other call its contents are meaningless. Returns SANTA_OK
+ * and writes *bytes, or a validation status. */
 santa_status santa_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes);
 
 /* Representative keys: reps[b][t][g][:] = the mean of the keys of team t of
