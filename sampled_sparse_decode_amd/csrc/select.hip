@@ -185,9 +185,12 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
                 // (independent draws), (j + u_0) / M (systematic) or
                 // (j + u_j) / M (stratified; [SAN]); team = first t with
                 // point * Z < C_t. j + u is exact in float64.
-                const uint4 r0 = philox4x32_10(make_uint4(0u, uint32_t(h), uint32_t(b), p.offset),
-                                               p.seed_lo, p.seed_hi);
-                const double u0 = (double(r0.x) + 0.5) * 0x1p-32;
+                double u0 = 0.0;                    // the systematic scheme's shared offset
+                if (p.scheme == SANTA_DRAW_SYSTEMATIC) {
+                    const uint4 r0 = philox4x32_10(make_uint4(0u, uint32_t(h), uint32_t(b), p.offset),
+                                                   p.seed_lo, p.seed_hi);
+                    u0 = (double(r0.x) + 0.5) * 0x1p-32;
+                }
                 for (int j = lane; j < p.M; j += 64) {
                     const uint4 r = philox4x32_10(make_uint4(uint32_t(j) >> 2, uint32_t(h), uint32_t(b), p.offset),
                                                   p.seed_lo, p.seed_hi);
