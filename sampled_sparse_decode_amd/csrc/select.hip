@@ -55,11 +55,12 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     __shared__ double c_s[kMaxTeams];              // cumulative sums of e within a wavefront's teams
     __shared__ float lnw_s[kMaxTeams];             // log weight of each team if drawn
     __shared__ float w_s[kMaxTeams];               // 1 / pi of each team if drawn
+    __shared__ double pts_s[kMaxTeams];            // draw points in [0, 1) (M < K <= kMaxTeams)
     __shared__ uint32_t bits_s[kMaxWords];
     __shared__ int32_t wpre_s[kMaxWords + 1];
     __shared__ int maxkey_s;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int bh = blockIdx.x;
     const int b = bh / p.Hq, h = bh - b * p.Hq, g = h / p.G;
     const KV *reps = static_cast<const KV *>(p.reps) + size_t(b) * p.P * p.Hkv * D;
@@ -77,6 +78,29 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
         const KV *r = reps + (size_t(row0 < p.P ? row0 : 0) * p.Hkv + g) * D + part * CPP * VPC;
 #pragma unroll
         for (int j = 0; j < CPP; ++j) raw[j] = ld16(r + j * VPC);
+    }
+    // Draw points, computed while the rows are in flight. Draw j's uniform is
+    // u_j = (x + 1/2) 2^-32 from Philox word j mod 4 of counter
+    // (j / 4, h, b, offset); its point is u_j (independent draws),
+    // (j + u_0) / M (systematic) or (j + u_j) / M (stratified; [SAN]).
+    // j + u is exact in float64. Not needed when M covers every team.
+    if (p.M < p.P) {
+        double u0 = 0.0;                          // the systematic scheme's shared offset
+        if (p.scheme == SANTA_DRAW_SYSTEMATIC) {
+            const uint4 r0 = philox4x32_10(make_uint4(0u, uint32_t(h), uint32_t(b), p.offset), p.seed_lo,
+                                           p.seed_hi);
+            u0 = (double(r0.x) + 0.5) * 0x1p-32;
+        }
+        for (int j = tid; j < p.M; j += kSel) {
+            const uint4 r = philox4x32_10(make_uint4(uint32_t(j) >> 2, uint32_t(h), uint32_t(b), p.offset),
+                                          p.seed_lo, p.seed_hi);
+            const uint32_t x = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
+            const double uj = (double(x) + 0.5) * 0x1p-32;
+            double point = uj;
+            if (p.scheme == SANTA_DRAW_SYSTEMATIC) point = (double(j) + u0) / double(p.M);
+            else if (p.scheme == SANTA_DRAW_STRATIFIED) point = (double(j) + uj) / double(p.M);
+            pts_s[j] = point;
+        }
     }
     const int L = clamp_len(Lraw, p.P * p.T);
     const int K = (L + p.T - 1) / p.T;
@@ -173,91 +197,73 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     for (int w = 0; w < kW; ++w) Z = wave_end(w, Z);
     const bool full = K > 0 && p.M >= K;
 
-    // 3. Wavefront 0 draws; the other wavefronts compute pi_t and log w_t for
-    //    every team meanwhile.
+    // 3. Draws: draw j (thread j, then j + 1024, ...) lands on the first team
+    //    t with target_j = point_j Z below C_t: the first wavefront range
+    //    whose end exceeds the target, then a binary search inside it. If no
+    //    team qualifies (unreachable for u < 1), the last team with mass.
+    //    Meanwhile the threads counted from the top compute pi_t and log w_t.
     if (K > 0) {
-        if (wave == 0) {
-            if (full) {
-                for (int t = lane; t < K; t += 64) atomicOr(&bits_s[t >> 5], 1u << (t & 31));
-            } else {
-                // Draw j's uniform: u_j = (x + 1/2) 2^-32 from Philox word
-                // j mod 4 of counter (j / 4, h, b, offset). Its point is u_j
-                // (independent draws), (j + u_0) / M (systematic) or
-                // (j + u_j) / M (stratified; [SAN]); team = first t with
-                // point * Z < C_t. j + u is exact in float64.
-                double u0 = 0.0;                    // the systematic scheme's shared offset
-                if (p.scheme == SANTA_DRAW_SYSTEMATIC) {
-                    const uint4 r0 = philox4x32_10(make_uint4(0u, uint32_t(h), uint32_t(b), p.offset),
-                                                   p.seed_lo, p.seed_hi);
-                    u0 = (double(r0.x) + 0.5) * 0x1p-32;
-                }
-                for (int j = lane; j < p.M; j += 64) {
-                    const uint4 r = philox4x32_10(make_uint4(uint32_t(j) >> 2, uint32_t(h), uint32_t(b), p.offset),
-                                                  p.seed_lo, p.seed_hi);
-                    const uint32_t x = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
-                    const double uj = (double(x) + 0.5) * 0x1p-32;
-                    double point = uj;
-                    if (p.scheme == SANTA_DRAW_SYSTEMATIC) point = (double(j) + u0) / double(p.M);
-                    else if (p.scheme == SANTA_DRAW_STRATIFIED) point = (double(j) + uj) / double(p.M);
-                    const double target = point * Z;
-                    int t;
-                    if (target < Z) {
-                        int w = 0;                      // first wavefront whose end exceeds the target
-                        double bw = 0.0;
-                        for (;; ++w) {
-                            const double next = wave_end(w, bw);
-                            if (target < next) break;
-                            bw = next;
-                        }
-                        int lo = min(K, w * 64 * per), hi = min(K, (w + 1) * 64 * per) - 1;
-                        while (lo < hi) {
-                            const int mid = (lo + hi) >> 1;
-                            if (target < bw + c_s[mid]) hi = mid; else lo = mid + 1;
-                        }
-                        t = lo;
-                    } else {        // unreachable for u < 1: last team with mass
-                        t = K - 1;
-                        while (t > 0 && !(e_s[t] > 0.0)) --t;
-                    }
-                    atomicOr(&bits_s[t >> 5], 1u << (t & 31));
-                }
-            }
+        if (full) {
+            for (int t = tid; t < K; t += kSel) atomicOr(&bits_s[t >> 5], 1u << (t & 31));
         } else {
-            // Inclusion probabilities. Independent: 1 - (1 - p)^M =
-            // -expm1(M log1p(-p)). Systematic: min(1, M p). Stratified: in
-            // units of 1/M the team covers [a, a + w), a = M C_(t-1) / Z,
-            // w = M p; it meets unit k = floor(a) over q1 = min(w, k + 1 - a)
-            // and the next units over r = w - q1, so pi = 1 if r >= 1 (a whole
-            // unit inside) else 1 - (1 - q1)(1 - r) = w - q1 r.
-            for (int t = tid - 64; t < K; t += kSel - 64) {
-                double lw = 0.0, w = 1.0;
-                if (!full) {
-                    const double pt_ = e_s[t] / Z;
-                    double pi;
-                    if (p.scheme == SANTA_DRAW_SYSTEMATIC) {
-                        pi = fmin(1.0, double(p.M) * pt_);
-                    } else if (p.scheme == SANTA_DRAW_STRATIFIED) {
-                        double cprev = 0.0;
-                        if (t > 0) {
-                            const int ww = (t - 1) / (64 * per);
-                            double bw = 0.0;
-                            for (int i = 0; i < ww; ++i) bw = wave_end(i, bw);
-                            cprev = bw + c_s[t - 1];
-                        }
-                        const double wd = double(p.M) * pt_;
-                        const double a = double(p.M) * cprev / Z;
-                        const double q1 = fmin(wd, (floor(a) + 1.0) - a);
-                        const double rest = wd - q1;
-                        pi = rest >= 1.0 ? 1.0 : wd - q1 * rest;
-                    } else {
-                        pi = -expm1(double(p.M) * log1p(-pt_));
+            for (int j = tid; j < p.M; j += kSel) {
+                const double target = pts_s[j] * Z;
+                int t;
+                if (target < Z) {
+                    int w = 0;                          // first wavefront whose end exceeds the target
+                    double bw = 0.0;
+                    for (;; ++w) {
+                        const double next = wave_end(w, bw);
+                        if (target < next) break;
+                        bw = next;
                     }
-                    w = 1.0 / pi;
-                    lw = -log(pi);
+                    int lo = min(K, w * 64 * per), hi = min(K, (w + 1) * 64 * per) - 1;
+                    while (lo < hi) {
+                        const int mid = (lo + hi) >> 1;
+                        if (target < bw + c_s[mid]) hi = mid; else lo = mid + 1;
+                    }
+                    t = lo;
+                } else {
+                    t = K - 1;
+                    while (t > 0 && !(e_s[t] > 0.0)) --t;
                 }
-                lnw_s[t] = float(lw);
-                w_s[t] = float(w);
+                atomicOr(&bits_s[t >> 5], 1u << (t & 31));
             }
+        }
+        // Inclusion probabilities. Independent: 1 - (1 - p)^M =
+        // -expm1(M log1p(-p)). Systematic: min(1, M p). Stratified: in units
+        // of 1/M the team covers [a, a + w), a = M C_(t-1) / Z, w = M p; it
+        // meets unit k = floor(a) over q1 = min(w, k + 1 - a) and the next
+        // units over r = w - q1, so pi = 1 if r >= 1 (a whole unit inside)
+        // else 1 - (1 - q1)(1 - r) = w - q1 r.
+        for (int t = kSel - 1 - tid; t < K; t += kSel) {
+            double lw = 0.0, w = 1.0;
+            if (!full) {
+                const double pt_ = e_s[t] / Z;
+                double pi;
+                if (p.scheme == SANTA_DRAW_SYSTEMATIC) {
+                    pi = fmin(1.0, double(p.M) * pt_);
+                } else if (p.scheme == SANTA_DRAW_STRATIFIED) {
+                    double cprev = 0.0;
+                    if (t > 0) {
+                        const int ww = (t - 1) / (64 * per);
+                        double bw = 0.0;
+                        for (int i = 0; i < ww; ++i) bw = wave_end(i, bw);
+                        cprev = bw + c_s[t - 1];
+                    }
+                    const double wd = double(p.M) * pt_;
+                    const double a = double(p.M) * cprev / Z;
+                    const double q1 = fmin(wd, (floor(a) + 1.0) - a);
+                    const double rest = wd - q1;
+                    pi = rest >= 1.0 ? 1.0 : wd - q1 * rest;
+                } else {
+                    pi = -expm1(double(p.M) * log1p(-pt_));
+                }
+                w = 1.0 / pi;
+                lw = -log(pi);
+            }
+            lnw_s[t] = float(lw);
+            w_s[t] = float(w);
         }
     }
     __syncthreads();
