@@ -26,12 +26,15 @@ namespace {
 
 using namespace dev;
 
-// One 1024-thread block per (sequence b, query head h) (16 wavefronts, four
-// per SIMD, so the float64 chains of one wavefront hide behind the others).
-// Writes the head's team bitmap and, for every drawn team t,
-// log w_t = -log(pi_t) (0 under full coverage), plus the optional sorted team
-// list and 1/pi.
+// One block per (sequence b, query head h): 1024 threads (16 wavefronts,
+// four per SIMD, so the float64 chains of one wavefront hide behind the
+// others; at about 120 registers one such block fills a CU), or 512 threads
+// when there are more heads than CUs, so that two blocks share a CU and
+// every head runs in the first round. Writes the head's team bitmap and, for
+// every drawn team t, log w_t = -log(pi_t) (0 under full coverage), plus the
+// optional sorted team list and 1/pi.
 constexpr int kSel = 1024;
+constexpr int kSelCUs = 256;                       // 1024-thread blocks that run at once (one per CU)
 constexpr int kParts = 4;                          // threads per representative row
 
 // Order-preserving map of a float to a signed integer (for LDS atomicMax).
@@ -44,11 +47,11 @@ __device__ __forceinline__ float key_float(int k) { return __int_as_float(k >= 0
 // PIPE: request each scoring pass's representative rows before the previous
 // pass is scored (chosen by the host when the page table allows more than
 // one pass; same arithmetic either way).
-template <typename KV, int D, bool PIPE>
-__global__ __launch_bounds__(kSel) void select_kernel(Params p) {
+template <typename KV, int D, bool PIPE, int NT>
+__global__ __launch_bounds__(NT, kSel / NT) void select_kernel(Params p) {
     constexpr int VPC = KVTraits<KV>::kPerChunk;
     constexpr int CPP = D / VPC / kParts;          // 16-byte chunks per thread and row
-    constexpr int ROWS = kSel / kParts;            // rows scored per pass
+    constexpr int ROWS = NT / kParts;            // rows scored per pass
     constexpr bool kPipe = PIPE && CPP <= 4;          // float32 rows at d = 128 do not fit the registers
     __shared__ double q_s[D];
     __shared__ double e_s[kMaxTeams];              // scores, then exp(s - m)
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
                                            p.seed_hi);
             u0 = (double(r0.x) + 0.5) * 0x1p-32;
         }
-        for (int j = tid; j < p.M; j += kSel) {
+        for (int j = tid; j < p.M; j += NT) {
             const uint4 r = philox4x32_10(make_uint4(uint32_t(j) >> 2, uint32_t(h), uint32_t(b), p.offset),
                                           p.seed_lo, p.seed_hi);
             const uint32_t x = (j & 3) == 0 ? r.x : (j & 3) == 1 ? r.y : (j & 3) == 2 ? r.z : r.w;
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     //    sums within each wavefront's range, so C_t = B_w + c_s[t] with B_w
     //    the sum of the previous wavefronts' last entries.
     const double m = double(key_float(maxkey_s));
-    const int per = (K + kSel - 1) / kSel;
+    const int per = (K + NT - 1) / NT;
     const int t0 = min(K, tid * per), t1 = min(K, t0 + per);
     double local = 0.0;
     for (int t = t0; t < t1; ++t) {
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     // Wavefront bases B_w = sum of the previous wavefronts' last cumulative
     // entries, added in wavefront order (the same way in every thread), so
     // C is one monotone sequence and Z = C_last.
-    constexpr int kW = kSel / 64;
+    constexpr int kW = NT / 64;
     auto wave_end = [&](int w, double bw) {
         const int lo = min(K, w * 64 * per), hi = min(K, (w + 1) * 64 * per);
         return hi > lo ? bw + c_s[hi - 1] : bw;
@@ -204,9 +207,9 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     //    Meanwhile the threads counted from the top compute pi_t and log w_t.
     if (K > 0) {
         if (full) {
-            for (int t = tid; t < K; t += kSel) atomicOr(&bits_s[t >> 5], 1u << (t & 31));
+            for (int t = tid; t < K; t += NT) atomicOr(&bits_s[t >> 5], 1u << (t & 31));
         } else {
-            for (int j = tid; j < p.M; j += kSel) {
+            for (int j = tid; j < p.M; j += NT) {
                 const double target = pts_s[j] * Z;
                 int t;
                 if (target < Z) {
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
         // meets unit k = floor(a) over q1 = min(w, k + 1 - a) and the next
         // units over r = w - q1, so pi = 1 if r >= 1 (a whole unit inside)
         // else 1 - (1 - q1)(1 - r) = w - q1 r.
-        for (int t = kSel - 1 - tid; t < K; t += kSel) {
+        for (int t = NT - 1 - tid; t < K; t += NT) {
             double lw = 0.0, w = 1.0;
             if (!full) {
                 const double pt_ = e_s[t] / Z;
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
     // 4. Outputs: bitmap, log weights of drawn teams, optional sorted list.
     if (tid < p.words) p.bitmaps[size_t(bh) * p.words + tid] = bits_s[tid];
     float *lnw = p.lnw + size_t(bh) * p.P;
-    for (int t = tid; t < K; t += kSel)
+    for (int t = tid; t < K; t += NT)
         if ((bits_s[t >> 5] >> (t & 31)) & 1u) lnw[t] = lnw_s[t];
     if (p.sampled) {
         if (tid == 0) {
@@ -283,14 +286,14 @@ __global__ __launch_bounds__(kSel) void select_kernel(Params p) {
             wpre_s[p.words] = acc;
         }
         __syncthreads();
-        for (int t = tid; t < K; t += kSel) {
+        for (int t = tid; t < K; t += NT) {
             const uint32_t word = bits_s[t >> 5];
             if (!((word >> (t & 31)) & 1u)) continue;
             const int rank = wpre_s[t >> 5] + __popc(word & ((1u << (t & 31)) - 1u));
             p.sampled[size_t(bh) * p.M + rank] = t;
             p.inv_pi[size_t(bh) * p.M + rank] = w_s[t];
         }
-        for (int r = wpre_s[p.words] + tid; r < p.M; r += kSel) {
+        for (int r = wpre_s[p.words] + tid; r < p.M; r += NT) {
             p.sampled[size_t(bh) * p.M + r] = -1;
             p.inv_pi[size_t(bh) * p.M + r] = 0.0f;
         }
@@ -319,25 +322,27 @@ __global__ __launch_bounds__(kBlock) void given_kernel(Params p) {
 
 }  // namespace
 
+template <typename KV, int D, int NT>
+static void launch_select_as(const Params &p, hipStream_t st, bool pipe) {
+    const dim3 grid(p.B * p.Hq);
+    if (pipe) hipLaunchKernelGGL((select_kernel<KV, D, true, NT>), grid, dim3(NT), 0, st, p);
+    else hipLaunchKernelGGL((select_kernel<KV, D, false, NT>), grid, dim3(NT), 0, st, p);
+}
+
+template <typename KV, int D>
+static void launch_select_d(const Params &p, hipStream_t st) {
+    if (int64_t(p.B) * p.Hq > kSelCUs) launch_select_as<KV, D, kSel / 2>(p, st, p.P > kSel / 2 / kParts);
+    else launch_select_as<KV, D, kSel>(p, st, p.P > kSel / kParts);   // pipe: more than one scoring pass
+}
+
 santa_status launch_select(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(p.B * p.Hq);
-    const bool pipe = p.P > kSel / kParts;          // more than one scoring pass possible
     if (p.dtype == SANTA_BF16) {
-        if (p.d == 64) {
-            if (pipe) hipLaunchKernelGGL((select_kernel<bf16_t, 64, true>), grid, dim3(kSel), 0, st, p);
-            else hipLaunchKernelGGL((select_kernel<bf16_t, 64, false>), grid, dim3(kSel), 0, st, p);
-        } else {
-            if (pipe) hipLaunchKernelGGL((select_kernel<bf16_t, 128, true>), grid, dim3(kSel), 0, st, p);
-            else hipLaunchKernelGGL((select_kernel<bf16_t, 128, false>), grid, dim3(kSel), 0, st, p);
-        }
+        if (p.d == 64) launch_select_d<bf16_t, 64>(p, st);
+        else launch_select_d<bf16_t, 128>(p, st);
     } else {
-        if (p.d == 64) {
-            if (pipe) hipLaunchKernelGGL((select_kernel<float, 64, true>), grid, dim3(kSel), 0, st, p);
-            else hipLaunchKernelGGL((select_kernel<float, 64, false>), grid, dim3(kSel), 0, st, p);
-        } else {
-            hipLaunchKernelGGL((select_kernel<float, 128, false>), grid, dim3(kSel), 0, st, p);
-        }
+        if (p.d == 64) launch_select_d<float, 64>(p, st);
+        else launch_select_d<float, 128>(p, st);
     }
     return launched();
 }
