@@ -26,13 +26,15 @@ namespace {
 
 using namespace dev;
 
-// One block per (sequence b, query head h): 1024 threads (16 wavefronts,
-// four per SIMD, so the float64 chains of one wavefront hide behind the
-// others; at about 120 registers one such block fills a CU), or 512 threads
-// when there are more heads than CUs, so that two blocks share a CU and
-// every head runs in the first round. Writes the head's team bitmap and, for
-// every drawn team t, log w_t = -log(pi_t) (0 under full coverage), plus the
-// optional sorted team list and 1/pi.
+// One block per (sequence b, query head h) of 512 or 1024 threads (8 or 16
+// wavefronts; at about 120 registers, four wavefronts per SIMD, so one
+// 1024-thread or two 512-thread blocks fill a CU and the float64 chains of
+// one wavefront hide behind the others). 512 threads when the page table has
+// at most 256 teams (two pipelined scoring passes measured faster than one
+// pass of twice the wavefronts) or when there are more heads than CUs (so
+// every head runs in the first round); 1024 threads otherwise. Writes the
+// head's team bitmap and, for every drawn team t, log w_t = -log(pi_t) (0
+// under full coverage), plus the optional sorted team list and 1/pi.
 constexpr int kSel = 1024;
 constexpr int kSelCUs = 256;                       // 1024-thread blocks that run at once (one per CU)
 constexpr int kParts = 4;                          // threads per representative row
@@ -48,7 +50,7 @@ __device__ __forceinline__ float key_float(int k) { return __int_as_float(k >= 0
 // pass is scored (chosen by the host when the page table allows more than
 // one pass; same arithmetic either way).
 template <typename KV, int D, bool PIPE, int NT>
-__global__ __launch_bounds__(NT, kSel / NT) void select_kernel(Params p) {
+__global__ __launch_bounds__(NT, 4) void select_kernel(Params p) {
     constexpr int VPC = KVTraits<KV>::kPerChunk;
     constexpr int CPP = D / VPC / kParts;          // 16-byte chunks per thread and row
     constexpr int ROWS = NT / kParts;            // rows scored per pass
@@ -331,8 +333,11 @@ static void launch_select_as(const Params &p, hipStream_t st, bool pipe) {
 
 template <typename KV, int D>
 static void launch_select_d(const Params &p, hipStream_t st) {
-    if (int64_t(p.B) * p.Hq > kSelCUs) launch_select_as<KV, D, kSel / 2>(p, st, p.P > kSel / 2 / kParts);
-    else launch_select_as<KV, D, kSel>(p, st, p.P > kSel / kParts);   // pipe: more than one scoring pass
+    const bool many_heads = int64_t(p.B) * p.Hq > kSelCUs;
+    const bool short_table = p.P <= kSel / kParts;
+    // pipe: more than one scoring pass
+    if (many_heads || short_table) launch_select_as<KV, D, kSel / 2>(p, st, p.P > kSel / 2 / kParts);
+    else launch_select_as<KV, D, kSel>(p, st, p.P > kSel / kParts);
 }
 
 santa_status launch_select(const Params &p, void *stream) {
