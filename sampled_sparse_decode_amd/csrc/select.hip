@@ -53,8 +53,8 @@ template <typename KV, int D, bool PIPE, int NT>
 __global__ __launch_bounds__(NT, 4) void select_kernel(Params p) {
     constexpr int VPC = KVTraits<KV>::kPerChunk;
     constexpr int CPP = D / VPC / kParts;          // 16-byte chunks per thread and row
-    constexpr int ROWS = NT / kParts;            // rows scored per pass
-    constexpr bool kPipe = PIPE && CPP <= 4;          // float32 rows at d = 128 do not fit the registers
+    constexpr int ROWS = NT / kParts;              // rows scored per pass
+    constexpr bool kPipe = PIPE && CPP <= 4;       // float32 rows at d = 128 do not fit the registers
     __shared__ double q_s[D];
     __shared__ double e_s[kMaxTeams];              // scores, then exp(s - m)
     __shared__ double c_s[kMaxTeams];              // cumulative sums of e within a wavefront's teams
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(Params p) {
     for (int w = 0; w < kW; ++w) Z = wave_end(w, Z);
     const bool full = K > 0 && p.M >= K;
 
-    // 3. Draws: draw j (thread j, then j + 1024, ...) lands on the first team
+    // 3. Draws: draw j (thread j, then j + NT, ...) lands on the first team
     //    t with target_j = point_j Z below C_t: the first wavefront range
     //    whose end exceeds the target, then a binary search inside it. If no
     //    team qualifies (unreachable for u < 1), the last team with mass.
