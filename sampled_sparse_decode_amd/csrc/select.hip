@@ -199,7 +199,12 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(Params p) {
         return hi > lo ? bw + c_s[hi - 1] : bw;
     };
     double Z = 0.0;
-    for (int w = 0; w < kW; ++w) Z = wave_end(w, Z);
+    double base[kW];                               // B_w, kept for the draws' first search step
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        base[w] = Z;
+        Z = wave_end(w, Z);
+    }
     const bool full = K > 0 && p.M >= K;
 
     // 3. Draws: draw j (thread j, then j + NT, ...) lands on the first team
@@ -215,13 +220,16 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(Params p) {
                 const double target = pts_s[j] * Z;
                 int t;
                 if (target < Z) {
-                    int w = 0;                          // first wavefront whose end exceeds the target
+                    // First wavefront whose end exceeds the target: the ends
+                    // are the next bases (non-decreasing; ranges fill in order),
+                    // so it is the number of bases B_1 .. B_(kW-1) <= target.
+                    int w = 0;
+#pragma unroll
+                    for (int i = 1; i < kW; ++i) w += base[i] <= target ? 1 : 0;
                     double bw = 0.0;
-                    for (;; ++w) {
-                        const double next = wave_end(w, bw);
-                        if (target < next) break;
-                        bw = next;
-                    }
+#pragma unroll
+                    for (int i = 0; i < kW; ++i)
+                        if (i == w) bw = base[i];
                     int lo = min(K, w * 64 * per), hi = min(K, (w + 1) * 64 * per) - 1;
                     while (lo < hi) {
                         const int mid = (lo + hi) >> 1;
@@ -262,6 +270,13 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(Params p) {
                     const double rest = wd - q1;
                     pi = rest >= 1.0 ? 1.0 : wd - q1 * rest;
                 } else {
+                    const float pf = float(pt_);
+                    if (pf >= 1e-30f) {                 // float32 (relative error below 1e-6)
+                        const float pif = -expm1f(float(p.M) * log1pf(-pf));
+                        lnw_s[t] = -logf(pif);
+                        w_s[t] = 1.0f / pif;
+                        continue;
+                    }
                     pi = -expm1(double(p.M) * log1p(-pt_));
                 }
                 w = 1.0 / pi;
