@@ -78,7 +78,12 @@ enumeration of all draw sequences on tiny inputs for unbiasedness of both
 sums and for P(t in S) = pi_t; Monte Carlo convergence over seeds; the
 expected set size against its closed form; chi-square of draw frequencies
 against p; invariants (constant values, permuted page tables); team scores
-with one-token teams against the attention weights of the library routine.
+with one-token teams against the attention weights of the library routine;
+the near-tie record on cumulative sums with exact binary boundaries (points
+just inside and just outside the band at each interior boundary, the last
+sum never a boundary, zero-mass neighbours, a team narrower than the band),
+with planted detector mistakes (band x1000 or /1000, teams off by one, the
+last sum taken as a boundary) each failing a pin.
 R9: the medoid of collinear keys is the median member (a skewed set
 separates it from the squared-distance choice), scipy's distance sums
 agree, ties go to the lowest index, translation invariance, outliers are
@@ -378,10 +383,37 @@ def inverse_cdf(u, e, C, Z):
 
 
 def draw_distance_to_boundary(u, C, Z):
-    """Distance from u to the nearest interior CDF boundary C_t / Z (t < K-1)."""
+    """Distance from u to the nearest interior CDF boundary C_t / Z (t < K-1).
+
+    C_(K-1) / Z = 1 lies above every point a draw can take, so it is never a
+    boundary a draw can cross."""
     if len(C) < 2:
         return math.inf
     return float(np.min(np.abs(u - C[:-1] / Z)))
+
+
+def near_tie_teams_of_draw(u, e, C, Z, band=None):
+    """Teams a draw at point u can land on when the normalised cumulative
+    sums C_t / Z move by less than `band` (NEAR_TIE by default).
+
+    Reading of the near-tie rule: an implementation whose team
+    probabilities differ by less than the band may send such a draw to any
+    team with positive mass whose interval [C_(t-1) / Z, C_t / Z) meets
+    (u - band, u + band). Teams with zero mass have empty intervals and are
+    never listed, so a boundary shared by several empty teams names the
+    teams on both sides that have mass. Returns that set when it holds two
+    or more teams (the draw is a near-tie), else the empty set.
+    """
+    band = NEAR_TIE if band is None else band
+    lo, hi = u - band, u + band
+    reach = set()
+    prev = 0.0
+    for t in range(len(C)):
+        right = C[t] / Z
+        if e[t] > 0 and prev < hi and right > lo:
+            reach.add(t)
+        prev = right
+    return reach if len(reach) >= 2 else set()
 
 
 DRAW_IID, DRAW_SYSTEMATIC, DRAW_STRATIFIED = 0, 1, 2
@@ -459,8 +491,9 @@ def select_teams(q_h, rep_rows, M, seed, offset, b, h, scheme=DRAW_IID):
 
     Draw j uses point u_j of draw_uniforms (Philox4x32-10; see oracle/philox.py
     for the counter layout) and takes team inverse_cdf(u_j). Draws whose
-    point lies within NEAR_TIE of a CDF boundary are recorded: both
-    neighbouring teams are listed in near_tie_teams.
+    point lies within NEAR_TIE of a CDF boundary are recorded: every team
+    with mass the draw could reach under such a shift is listed in
+    near_tie_teams (near_tie_teams_of_draw).
     """
     K = len(rep_rows)
     s = rep_scores(q_h, rep_rows)
@@ -473,9 +506,7 @@ def select_teams(q_h, rep_rows, M, seed, offset, b, h, scheme=DRAW_IID):
     for u in draw_uniforms(scheme, M, seed, offset, b, h):
         t = inverse_cdf(u, e, C, Z)
         draws.append(t)
-        if draw_distance_to_boundary(u, C, Z) < NEAR_TIE:
-            k = int(np.argmin(np.abs(u - C[:-1] / Z)))
-            near.update((k, k + 1))
+        near.update(near_tie_teams_of_draw(u, e, C, Z))
     teams = sorted(set(draws))
     pi = [inclusion_probability_scheme(scheme, t, C, Z, p, M) for t in teams]
     sel = Selection(teams, pi, p, near, draws, False)

@@ -4,8 +4,13 @@ same seeded inputs and compare the HIP results with it, head by head.
 Tolerances (max-abs over every output element): 4e-3 for a bfloat16 cache
 with float32 accumulation, 1e-5 for a float32 cache. Team sets must match
 exactly, except that a draw whose uniform lies within 1e-6 of a CDF boundary
-(a near-tie, flagged by the oracle) may land on either neighbouring team;
+(a near-tie, flagged by the oracle) may land on another team it can reach;
 then the HIP output is compared with the oracle's estimate on the HIP set.
+
+The log-sum-exp is a float32 output with no tolerance of its own in the
+method's statement: it is held to the output tolerance plus four float32
+roundings of its own magnitude (the shift, the sum of exponentials, the
+logarithm and the final add each round once), i.e. OUT_TOL + 4 * 2^-24 * |lse|.
 """
 import math
 
@@ -15,7 +20,9 @@ from oracle import numerics, santa
 
 OUT_TOL = {"bf16": 4e-3, "f32": 1e-5}
 LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}
+LSE_RTOL = 4 * 2.0 ** -24
 INV_PI_RTOL = 1e-6
+MAX_FLIPS = 1          # near-tie flips allowed per workload (selection is float64: expected ~0)
 
 
 def oracle_kv(w):
@@ -59,7 +66,8 @@ def _check_lse(w, got, ref, b, h):
     if ref == -math.inf:
         assert got == -math.inf, f"(b={b}, h={h}) lse {got}, expected -inf"
     else:
-        assert abs(got - ref) <= LSE_TOL[w.dtype] * max(1.0, abs(ref) / 16), f"(b={b}, h={h}) lse {got} vs {ref}"
+        tol = LSE_TOL[w.dtype] + LSE_RTOL * abs(ref)
+        assert abs(got - ref) <= tol, f"(b={b}, h={h}) lse {got} vs {ref} (tolerance {tol:.3g})"
 
 
 def check_santa_head(w, kv, reps, b, h, out, lse, teams, inv_pi, M=None, seed=None, offset=None,

@@ -251,6 +251,91 @@ def test_inverse_cdf_never_picks_zero_mass():
         assert santa.inverse_cdf(u, e, C, C[-1]) in (1, 4)
 
 
+# Near-tie record. A draw whose point lies within 1e-6 of a boundary C_t / Z
+# may land on another team in an implementation whose probabilities differ
+# by less than that; the GPU parity tests accept set differences only inside
+# the oracle's record, so the record is pinned here on cumulative sums whose
+# boundaries are exact binary fractions.
+
+def _near_tie_pin_failures(fn):
+    """Failures of a near-tie detector fn(u, e, C, Z) -> set on hand-built
+    cumulative sums (an empty list when it passes every pin)."""
+    bad = []
+
+    def check(name, u, e, want):
+        e = np.asarray(e, dtype=np.float64)
+        C = np.cumsum(e)
+        got = set(fn(u, e, C, C[-1]))
+        if got != set(want):
+            bad.append((name, u, sorted(got), sorted(want)))
+
+    e = [1.0, 2.0, 3.0, 2.0]                       # boundaries 1/8, 3/8, 3/4 (exact)
+    for t, b in enumerate((0.125, 0.375, 0.75)):
+        for du in (-5e-7, 5e-7, -9.5e-7, 9.5e-7):
+            check(f"inside band at boundary {t}", b + du, e, {t, t + 1})
+        for du in (-2e-6, 2e-6, -1.05e-6, 1.05e-6):
+            check(f"outside band at boundary {t}", b + du, e, set())
+    check("mid-team", 0.25, e, set())
+    check("near 0", 5e-7, e, set())
+    check("C_last / Z = 1 is not a boundary", 1.0 - 5e-7, e, set())
+    check("C_last / Z = 1 is not a boundary (closer)", 1.0 - 2.0 ** -33, e, set())
+    # zero-mass teams between two teams with mass: the boundary at 1/2 is
+    # shared by teams 0, 1 and 2; the reachable teams are 0 and 3
+    for du in (-5e-7, 5e-7):
+        check("zero-mass neighbours", 0.5 + du, [1.0, 0.0, 0.0, 1.0], {0, 3})
+    check("zero-mass neighbours, outside band", 0.5 + 3e-6, [1.0, 0.0, 0.0, 1.0], set())
+    # a team narrower than the band: all three teams reachable
+    check("narrow middle team", 0.5 + 2.0 ** -22, [2.0 ** 20, 1.0, 2.0 ** 20 - 1], {0, 1, 2})
+    return bad
+
+
+def test_near_tie_record_pins():
+    assert _near_tie_pin_failures(santa.near_tie_teams_of_draw) == []
+
+
+def _old_argmin_detector(u, e, C, Z):
+    # the earlier record: nearest interior boundary k by argmin, teams (k, k + 1)
+    if santa.draw_distance_to_boundary(u, C, Z) < santa.NEAR_TIE:
+        k = int(np.argmin(np.abs(u - C[:-1] / Z)))
+        return {k, k + 1}
+    return set()
+
+
+def _with_last_boundary(u, e, C, Z):
+    # treats C_last / Z = 1 as a boundary a draw could cross
+    r = set(santa.near_tie_teams_of_draw(u, e, C, Z))
+    if abs(u - 1.0) < santa.NEAR_TIE:
+        r |= {len(C) - 1, len(C)}
+    return r
+
+
+@pytest.mark.parametrize("mutant", [
+    lambda u, e, C, Z: santa.near_tie_teams_of_draw(u, e, C, Z, band=santa.NEAR_TIE * 1000),   # threshold x 1000
+    lambda u, e, C, Z: santa.near_tie_teams_of_draw(u, e, C, Z, band=santa.NEAR_TIE / 1000),   # threshold / 1000
+    lambda u, e, C, Z: {t + 1 for t in santa.near_tie_teams_of_draw(u, e, C, Z)},            # teams off by one
+    lambda u, e, C, Z: {t - 1 for t in santa.near_tie_teams_of_draw(u, e, C, Z)},
+    _old_argmin_detector,
+    _with_last_boundary,
+], ids=["band_x1000", "band_div1000", "plus_one", "minus_one", "argmin_pair", "last_boundary"])
+def test_near_tie_pins_catch_planted_mistakes(mutant):
+    assert _near_tie_pin_failures(mutant) != []
+
+
+def test_select_teams_records_near_tie_draws(monkeypatch):
+    # Scores chosen so the team softmax has boundaries near 1/8, 3/8, 3/4; the
+    # draw points are placed by hand beside the second boundary.
+    s = np.log(np.array([1.0, 2.0, 3.0, 2.0]))
+    rep_rows = np.diag(np.ones(4)) * 0.0
+    e, C, Z, p = santa.team_softmax(s)
+    b1 = C[1] / Z
+    pts = [b1 - 4e-7, 0.9, b1 + 3e-6]
+    monkeypatch.setattr(santa, "draw_uniforms", lambda scheme, M, seed, offset, b, h: pts)
+    monkeypatch.setattr(santa, "rep_scores", lambda q_h, rows: s)
+    sel = santa.select_teams(np.zeros(4), rep_rows, 3, 0, 0, 0, 0)
+    assert sel.draws == [1, 3, 2]
+    assert sel.near_tie_teams == {1, 2}
+
+
 def test_draw_frequencies_chi_square():
     from scipy.stats import chisquare
     rng = np.random.default_rng(11)
