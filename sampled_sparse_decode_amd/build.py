@@ -38,18 +38,27 @@ def hipcc():
     return exe
 
 
-def build(verbose=False):
-    """Compile every source and link libsanta.so; returns its path."""
+def build(verbose=False, jobs=None):
+    """Compile every source (in parallel, `jobs` at a time) and link
+    libsanta.so; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmds.append([hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    jobs = jobs or min(len(cmds), os.cpu_count() or 1, 8)
+
+    def compile_one(cmd):
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
+
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(compile_one, c) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
