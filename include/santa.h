@@ -22,7 +22,9 @@
  *           caller, 16-byte aligned, densely packed in the layout stated.
  *           The library allocates nothing and keeps no state between calls;
  *           calls are re-entrant and may run concurrently on different
- *           streams if their output and workspace buffers differ.
+ *           streams if their output and workspace buffers differ. (The one
+ *           exception, santa_decode_attention_noalloc, brings its own
+ *           workspace: a device array per GPU, shared by its calls.)
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  *           stream). All work is enqueued on it and the call returns before
  *           it runs; buffers must stay valid until the stream reaches it.
@@ -210,6 +212,31 @@ santa_status santa_decode_attention(const santa_kv *kv, const void *q, const voi
                                     int32_t M, uint64_t seed, uint32_t offset,
                                     float *out, float *lse, int32_t *sampled, float *inv_pi,
                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* santa_decode_attention without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments (minus workspace),
+ * same draws and same results bit for bit as santa_decode_attention.
+ * The workspace is a file-scope device array of SANTA_NOALLOC_SCRATCH_BYTES
+ * that each GPU the library runs on holds until the process ends; this call
+ * allocates nothing (no hipMalloc or hipFree, no allocating library call).
+ * Sizing: a workspace with one partial slot per split-K block of this call,
+ *   B*Hq*ceil(P/32)*4 + B*Hq*P*4 + B*Hq*S*8 + B*Hq*S*d*4 + B*Hkv*4 bytes,
+ *   each term rounded up to 256, with S the call's split count (bfloat16:
+ *   min(P, ceil(256 / (B*Hkv)))); a shape that needs more than the array
+ *   returns SANTA_ERR_WORKSPACE and enqueues nothing.
+ * Device: the array of the device that owns `stream` (the current device for
+ *   the NULL stream); its address is looked up once per device, on the first
+ *   call there.
+ * Sharing: every call on one GPU uses that GPU's array, whose contents the
+ *   next call overwrites (nothing in it needs initialising). Calls that
+ *   overlap on one GPU (other streams, other host threads) race on it and
+ *   give meaningless results; serialise them on one stream. */
+#define SANTA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+santa_status santa_decode_attention_noalloc(const santa_kv *kv, const void *q, const void *reps,
+                                            int32_t M, uint64_t seed, uint32_t offset,
+                                            float *out, float *lse, int32_t *sampled, float *inv_pi,
+                                            void *stream);
 
 /* Where the M draws of santa_decode_attention_ex / santa_select_teams_ex
  * fall. The SANTA page ("Stochastic Sparse Attention for Memory-Bound

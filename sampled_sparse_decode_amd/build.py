@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsanta.so")
 ARCH = "gfx950"
 
-SOURCES = ["santa_api.cpp", "reps.hip", "select.hip", "gather.hip", "pack.hip", "cluster.hip"]
+SOURCES = ["santa_api.cpp", "reps.hip", "select.hip", "gather.hip", "pack.hip", "cluster.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -30,11 +30,16 @@ santa_status validate_kv(const santa_kv *kv) {
 }
 
 WorkspaceLayout workspace_layout(const santa_kv &kv) {
+    return workspace_layout(kv, kv.dtype == SANTA_BF16 ? std::max<int32_t>(kv.max_pages_per_seq, kSpreadBlocks)
+                                                       : kv.max_pages_per_seq);
+}
+
+WorkspaceLayout workspace_layout(const santa_kv &kv, int32_t slots) {
     WorkspaceLayout w{};
     const size_t B = kv.batch, Hq = kv.num_q_heads, P = kv.max_pages_per_seq, d = kv.head_dim;
     w.words = (kv.max_pages_per_seq + 31) / 32;
     w.max_splits = kv.max_pages_per_seq;
-    w.slots = kv.dtype == SANTA_BF16 ? std::max<int32_t>(kv.max_pages_per_seq, kSpreadBlocks) : kv.max_pages_per_seq;
+    w.slots = slots;
     const size_t S = size_t(w.slots);
     size_t off = 0;
     w.bitmaps = off;   off = align256(off + B * Hq * size_t(w.words) * 4);
@@ -93,10 +98,9 @@ static void santa_split(Params *p) {
     p->max_splits = int32_t((U + p->tps - 1) / p->tps);
 }
 
-static Params base_params(const santa_kv &kv, const void *q, float *out, float *lse,
-                          void *workspace) {
+static Params base_params(const santa_kv &kv, const void *q, float *out, float *lse, void *workspace,
+                          const WorkspaceLayout &w) {
     Params p{};
-    const WorkspaceLayout w = workspace_layout(kv);
     p.dtype = kv.dtype;
     p.k_pages = kv.k_pages;
     p.v_pages = kv.v_pages;
@@ -125,6 +129,10 @@ static Params base_params(const santa_kv &kv, const void *q, float *out, float *
     p.out = out;
     p.lse = lse;
     return p;
+}
+
+static Params base_params(const santa_kv &kv, const void *q, float *out, float *lse, void *workspace) {
+    return base_params(kv, q, out, lse, workspace, workspace_layout(kv));
 }
 
 static santa_status check_workspace(const santa_kv &kv, void *workspace, size_t bytes) {
@@ -268,6 +276,41 @@ santa_status santa_decode_attention_ex(const santa_kv *kv, const void *q, const 
                                stream);
     if (st != SANTA_OK) return st;
     return santa_attend_selected(kv, q, M, out, lse, workspace, workspace_bytes, stream);
+}
+
+santa_status santa_decode_attention_noalloc(const santa_kv *kv, const void *q, const void *reps,
+                                            int32_t M, uint64_t seed, uint32_t offset,
+                                            float *out, float *lse, int32_t *sampled, float *inv_pi,
+                                            void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!q || !reps || !out) return SANTA_ERR_NULL;
+    if (M < 1) return SANTA_ERR_SHAPE;
+    if ((sampled == nullptr) != (inv_pi == nullptr)) return SANTA_ERR_NULL;
+    // The split shape of this call, then a workspace with exactly its slots.
+    Params p = base_params(*kv, q, out, lse, nullptr);
+    p.M = M;
+    p.mode = kModeSanta;
+    santa_split(&p);
+    const WorkspaceLayout w = workspace_layout(*kv, p.max_splits);
+    if (w.total > kNoallocScratchBytes) return SANTA_ERR_WORKSPACE;
+    void *scratch = nullptr;
+    st = noalloc_scratch(stream, &scratch);
+    if (st != SANTA_OK) return st;
+    Params r = base_params(*kv, q, out, lse, scratch, w);
+    r.M = M;
+    r.mode = kModeSanta;
+    santa_split(&r);
+    r.scheme = SANTA_DRAW_IID;
+    r.reps = reps;
+    r.seed_lo = uint32_t(seed & 0xffffffffu);
+    r.seed_hi = uint32_t(seed >> 32);
+    r.offset = offset;
+    r.sampled = sampled;
+    r.inv_pi = inv_pi;
+    st = launch_select(r, stream);
+    if (st != SANTA_OK) return st;
+    return run_gather_combine(r, stream);
 }
 
 santa_status santa_decode_attention(const santa_kv *kv, const void *q, const void *reps,

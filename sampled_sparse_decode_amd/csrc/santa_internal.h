@@ -37,6 +37,15 @@ constexpr int kSpreadBlocks = 256;
 constexpr int kMaxSpreadGroups = 256;
 
 WorkspaceLayout workspace_layout(const santa_kv &kv);
+// The same sections with `slots` partial slots per head (the splits one
+// launch uses), for a workspace sized to a single call.
+WorkspaceLayout workspace_layout(const santa_kv &kv, int32_t slots);
+
+// Device scratch of santa_decode_attention_noalloc (noalloc.hip): the
+// address of the file-scope array on the device of `stream` (the current
+// device for the NULL stream), looked up once per device.
+constexpr size_t kNoallocScratchBytes = SANTA_NOALLOC_SCRATCH_BYTES;
+santa_status noalloc_scratch(void *stream, void **ptr);
 
 // Everything a kernel launch needs, passed by value.
 struct Params {

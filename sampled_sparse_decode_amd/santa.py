@@ -25,6 +25,7 @@ EXPORTED = (
     "santa_build_reps_ex",
     "santa_decode_attention",
     "santa_decode_attention_ex",
+    "santa_decode_attention_noalloc",
     "santa_select_teams",
     "santa_select_teams_ex",
     "santa_attend_selected",
@@ -86,6 +87,7 @@ def load():
         "santa_build_reps_ex": (i32, [kvp, P, i32, u64, P, i32, P]),
         "santa_decode_attention": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P, sz, P]),
         "santa_decode_attention_ex": (i32, [kvp, P, P, i32, u64, u32, i32, P, P, P, P, P, sz, P]),
+        "santa_decode_attention_noalloc": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P]),
         "santa_select_teams": (i32, [kvp, P, P, i32, u64, u32, P, P, P, sz, P]),
         "santa_select_teams_ex": (i32, [kvp, P, P, i32, u64, u32, i32, P, P, P, sz, P]),
         "santa_attend_selected": (i32, [kvp, P, i32, P, P, P, sz, P]),
@@ -454,6 +456,29 @@ def _decode(kv, q, reps, M, seed, offset, scheme, workspace, out, lse, return_se
     if return_sets:
         return out, lse, sampled, inv_pi
     return out, lse
+
+
+def santa_decode_attention_noalloc(kv, q, reps, M, seed=0, offset=0, out=None, lse=None, sampled=None,
+                                   inv_pi=None):
+    """santa_decode_attention on the library's own device scratch (no workspace
+    argument; the call allocates nothing). Outputs not given are allocated
+    here, before the call. Returns (out, lse, sampled, inv_pi); the last two
+    are None unless given."""
+    _check_q(kv, q)
+    _check_reps(kv, reps)
+    _check_outputs(kv, out, lse)
+    _check_sets(kv, M, sampled, inv_pi)
+    B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=kv.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=kv.device)
+    desc = kv.desc()
+    st = load().santa_decode_attention_noalloc(ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), int(seed),
+                                               int(offset), _ptr(out), _ptr(lse), _ptr(sampled), _ptr(inv_pi),
+                                               _stream())
+    _check("santa_decode_attention_noalloc", st)
+    return out, lse, sampled, inv_pi
 
 
 def santa_select_teams(kv, q, reps, M, seed, offset, workspace, sampled=None, inv_pi=None):

@@ -131,6 +131,24 @@ def test_decode_argument_checks(lib):
     assert lib.santa_build_reps(ctypes.byref(k), None, None) == NULL
 
 
+def test_noalloc_decode_argument_checks(lib):
+    # Every rejection happens before the scratch lookup (no HIP call).
+    f = lib.santa_decode_attention_noalloc
+    k = kv()
+    assert f(ctypes.byref(k), None, FAKE, 31, 0, 0, FAKE, None, None, None, None) == NULL
+    assert f(ctypes.byref(k), FAKE, None, 31, 0, 0, FAKE, None, None, None, None) == NULL
+    assert f(ctypes.byref(k), FAKE, FAKE, 31, 0, 0, None, None, None, None, None) == NULL
+    assert f(ctypes.byref(k), FAKE, FAKE, 0, 0, 0, FAKE, None, None, None, None) == SHAPE
+    assert f(ctypes.byref(k), FAKE, FAKE, 31, 0, 0, FAKE, None, FAKE, None, None) == NULL
+    assert f(None, FAKE, FAKE, 31, 0, 0, FAKE, None, None, None, None) == NULL
+    bad = kv(head_dim=96)
+    assert f(ctypes.byref(bad), FAKE, FAKE, 31, 0, 0, FAKE, None, None, None, None) == UNSUP
+    # A shape whose single-call workspace exceeds the 64 MiB device array:
+    # the log-weights alone are 4096 * 28 * 2048 * 4 bytes.
+    big = kv(batch=4096, max_pages_per_seq=2048)
+    assert f(ctypes.byref(big), FAKE, FAKE, 31, 0, 0, FAKE, None, None, None, None) == WS
+
+
 def test_pack_pages_validation(lib):
     """santa_pack_pages rejects bad arguments on the host, before any launch."""
     F = ctypes.c_void_p
