@@ -33,7 +33,7 @@
 // channel-major [d][32 tokens] inside a chunk. Every 16-byte load of a
 // matrix-core operand then sits in a run of whole 128-byte lines that the
 // same instruction reads completely.
-#include "device_common.h"
+#include "selection.h"
 
 namespace santa {
 namespace {
@@ -344,18 +344,19 @@ __device__ __forceinline__ void mfma_compute_chunk_at(const Params &p, int n, in
 
 // Cross-wavefront merge of the online-softmax states and the store of the
 // block's partial at slot s of every head of the group.
-template <int D>
+template <int D, int NW = kWaves>
 struct MfmaReduce {
-    float m[kWaves][kGM];
-    float l[kWaves][kGM];
-    float o[kWaves][kGM][D];
-    float fac[kGM][kWaves];
+    float m[NW][kGM];
+    float l[NW][kGM];
+    float o[NW][kGM][D];
+    float fac[kGM][NW];
     float hm[kGM], hl[kGM];
 };
 
-template <int D>
-__device__ __forceinline__ void mfma_store_partial(const Params &p, MfmaReduce<D> &rd, float m, float lsum,
+template <int D, int NW = kWaves>
+__device__ __forceinline__ void mfma_store_partial(const Params &p, MfmaReduce<D, NW> &rd, float m, float lsum,
                                                    const f32x4 (&o)[D / 16], int hbase, int s) {
+    constexpr int NTH = NW * 64;
     constexpr int NT = D / 16;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, g4 = lane >> 4;
@@ -379,9 +380,9 @@ __device__ __forceinline__ void mfma_store_partial(const Params &p, MfmaReduce<D
     if (tid < G) {
         const int h = tid;
         float mx = rd.m[0][h];
-        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, rd.m[w][h]);
+        for (int w = 1; w < NW; ++w) mx = fmaxf(mx, rd.m[w][h]);
         float l = 0.0f;
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float f = (rd.m[w][h] == kNegInfF) ? 0.0f : expf(rd.m[w][h] - mx);
             rd.fac[h][w] = f;
             l += f * rd.l[w][h];
@@ -391,7 +392,7 @@ __device__ __forceinline__ void mfma_store_partial(const Params &p, MfmaReduce<D
     }
     __syncthreads();
     float2 *part_ml = reinterpret_cast<float2 *>(p.part_ml);
-    for (int idx = tid; idx < G * D; idx += kBlock) {
+    for (int idx = tid; idx < G * D; idx += NTH) {
         const int h = idx / D, c = idx - h * D;
         const size_t slot = size_t(hbase + h) * p.slots + s;
         if (rd.hm[h] == kNegInfF) {                 // no team of this block for the head
@@ -400,7 +401,7 @@ __device__ __forceinline__ void mfma_store_partial(const Params &p, MfmaReduce<D
         }
         float a = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) a += rd.fac[h][w] * rd.o[w][h][c];
+        for (int w = 0; w < NW; ++w) a += rd.fac[h][w] * rd.o[w][h][c];
         p.part_acc[slot * D + c] = a;
         if (c == 0) part_ml[slot] = make_float2(rd.hm[h], rd.hl[h]);
     }
@@ -432,18 +433,20 @@ __device__ __forceinline__ void fill_q_lds(const Params &p, bf16_t (*q_lds)[D + 
 // ---------------------------------------------------------------------------
 constexpr int kWin = 64;
 
-struct GroupChunks {
-    uint32_t hbits[kGM][kMaxWords];        // team bitmaps of the group's heads
-    uint32_t uword[kMaxWords];             // their union
-    int32_t upre[kMaxWords + 1];           // exclusive prefix of the union popcounts
+template <int MAXT = kMaxTeams, int MAXG = kGM>
+struct GroupChunksT {
+    uint32_t hbits[MAXG][MAXT / 32];       // team bitmaps of the group's heads
+    uint32_t uword[MAXT / 32];             // their union
+    int32_t upre[MAXT / 32 + 1];           // exclusive prefix of the union popcounts
     int32_t len;                           // clamped sequence length
-    int32_t pt[kMaxTeams];                 // the sequence's page-table row
+    int32_t pt[MAXT];                      // the sequence's page-table row
     int64_t page[kWin];
     int32_t n[kWin];                       // valid tokens of the chunk's team
     int32_t tb[kWin];                      // first token of the chunk within its team
     int32_t team[kWin];
     uint32_t mask[kWin];                   // heads that drew the chunk's team
 };
+using GroupChunks = GroupChunksT<>;
 
 // Round trip 1 and the union: words, popcount prefix; returns the union size.
 __device__ __forceinline__ void group_load(const Params &p, GroupChunks &gc, int g, int b) {
@@ -464,7 +467,8 @@ __device__ __forceinline__ void group_load(const Params &p, GroupChunks &gc, int
 
 // The union words and their popcount prefix from the loaded group data;
 // returns the union size.
-__device__ __forceinline__ int group_scan(const Params &p, GroupChunks &gc) {
+template <class GC>
+__device__ __forceinline__ int group_scan(const Params &p, GC &gc) {
     const int tid = threadIdx.x;
     const int G = p.G;
     const bool dense = p.mode == kModeDense;
@@ -502,7 +506,8 @@ __device__ int group_union(const Params &p, GroupChunks &gc, int g, int b) {
 
 // Chunks c0 .. c0 + cnt - 1 (cnt <= kWin) of the group: team, heads, page,
 // size, from LDS only.
-__device__ void chunk_window(const Params &p, GroupChunks &gc, int cpt, int c0, int cnt) {
+template <class GC>
+__device__ void chunk_window(const Params &p, GC &gc, int cpt, int c0, int cnt) {
     const int tid = threadIdx.x;
     const int G = p.G;
     if (tid < cnt) {
@@ -576,6 +581,431 @@ __global__ __launch_bounds__(kBlock, 3) void gather_balanced_kernel(Params p) {
         __syncthreads();                          // the window is reused
     }
     mfma_store_partial<D>(p, lds.rd, m, lsum, o, hbase, j);
+}
+
+// ---------------------------------------------------------------------------
+// SANTA++ gather over a group's union (bf16) on NW wavefronts per block: the
+// block reads the team bitmaps and log weights the selection kernel left in
+// the workspace and streams the group's union chunks in even contiguous
+// ranges, one per block, exactly as the balanced gather above.
+// Blocks are placed by XCD: consecutive (group, range) slots go to the same
+// XCD (block i runs on XCD i mod 8), so the blocks of one group share the
+// group's metadata in one or two L2 caches.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+struct UnionGatherLds {
+    struct Live {
+        GroupChunksT<kMaxTeams, kGM> gc;
+        __attribute__((aligned(16))) bf16_t q_lds[kGM][D + 8];
+    };
+    union {
+        Live live;
+        MfmaReduce<D, NW> rd;                     // used once the chunk loop is done
+    };
+};
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void santa_gather_kernel(Params p) {
+    constexpr int NT = D / 16;
+    constexpr int NTH = NW * 64;
+    __shared__ UnionGatherLds<D, NW> lds;
+    auto &gc = lds.live.gc;
+
+    // Block -> (group, range) slot: XCD x = i mod 8 takes slots
+    // [x n8, (x + 1) n8) of the n8 = gridDim.x / 8 per XCD.
+    const int nb = p.max_splits;
+    const int nreal = p.B * p.Hkv * nb;
+    const int slot = int(blockIdx.x & 7) * int(gridDim.x >> 3) + int(blockIdx.x >> 3);
+    if (slot >= nreal) return;
+    const int grp = slot / nb, j = slot - grp * nb;
+    const int b = grp / p.Hkv, g = grp - b * p.Hkv;
+    const int hbase = b * p.Hq + g * p.G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i16 = lane & 15, g4 = lane >> 4;
+
+    // Round trip 1: length, queries, the page-table row and the heads'
+    // bitmaps, all requested before any is used.
+    const int Lraw = p.seq_lens[b];
+    const int qh = tid >> 4, qc = tid & 15;                 // 16 head slots x 16 pieces of 16 bytes
+    uint4 qv = make_uint4(0, 0, 0, 0);
+    if (tid < 256 && qc * 8 < D && qh < p.G)
+        qv = ld16(static_cast<const bf16_t *>(p.q) + size_t(hbase + qh) * D + qc * 8);
+    constexpr int PTN = kMaxTeams / NTH, BWN = kGM * kMaxWords / NTH;
+    int32_t ptv[PTN];
+    uint32_t bwv[BWN];
+#pragma unroll
+    for (int k = 0; k < PTN; ++k) {
+        const int t = tid + k * NTH;
+        ptv[k] = t < p.P ? p.page_table[size_t(b) * p.P + t] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < BWN; ++k) {
+        const int idx = tid + k * NTH;
+        const int h = idx / p.words, w = idx - h * p.words;
+        bwv[k] = idx < p.G * p.words ? p.bitmaps[size_t(hbase + h) * p.words + w] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < PTN; ++k)
+        if (tid + k * NTH < p.P) gc.pt[tid + k * NTH] = ptv[k];
+#pragma unroll
+    for (int k = 0; k < BWN; ++k) {
+        const int idx = tid + k * NTH;
+        if (idx < p.G * p.words) gc.hbits[idx / p.words][idx % p.words] = bwv[k];
+    }
+    if (tid < 256 && qc * 8 < D) *reinterpret_cast<uint4 *>(&lds.live.q_lds[qh][qc * 8]) = qv;
+    if (tid == 0) gc.len = clamp_len(Lraw, p.P * p.T);
+    __syncthreads();
+
+    const int U = group_scan(p, gc);
+    const int cpt = p.T >= 32 ? p.T / 32 : 1;
+    const int total = U * cpt;
+    const int c0 = int((long long)total * j / nb), c1 = int((long long)total * (j + 1) / nb);
+
+    float m = kNegInfF, lsum = 0.0f;
+    f32x4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *lnw_h = p.lnw + size_t(hbase + i16) * p.P;
+    for (int w0 = c0; w0 < c1; w0 += kWin) {
+        const int cnt = min(kWin, c1 - w0);
+        chunk_window(p, gc, cpt, w0, cnt);
+        for (int q = wave; q < cnt; q += NW) {
+            const bool drew = (gc.mask[q] >> i16) & 1u;
+            const float lw_raw = drew ? lnw_h[gc.team[q]] : 0.0f;
+            MfmaChunk<D> ck;
+            mfma_load_chunk_at<D>(p, gc.page[q], gc.n[q], gc.tb[q], g, i16, g4, ck);
+            const float lw = drew ? lw_raw : kNegInfF;
+            mfma_compute_chunk_at<D>(p, gc.n[q], gc.tb[q], lw, i16, g4, lds.live.q_lds, ck, m, lsum, o);
+        }
+        __syncthreads();                          // the window is reused
+    }
+    mfma_store_partial<D, NW>(p, lds.rd, m, lsum, o, hbase, j);
+}
+
+// ---------------------------------------------------------------------------
+// Per-head SANTA++ gather (bf16), for calls with few query heads: block
+// (b, h, j) takes the j-th of S even ranges of head h's drawn chunks (the
+// 32-token pieces of the teams head h drew, in team order) and runs the
+// weighted online softmax for that head alone on the vector ALUs.
+//   FUSED  the block first selects head h's teams itself (selection.h, the
+//          same arithmetic as the selection kernel), so a decode call is this
+//          kernel and the combine;
+//   else   it reads the head's bitmap and log weights from the workspace
+//          (santa_attend_selected after santa_select_teams).
+// A team that several heads of a group drew is read by each of them; the
+// blocks of one (group, range) are placed on the same XCD (consecutive
+// slots, block i on XCD i mod 8) so that such repeated reads of a tile meet
+// in that XCD's L2. Keys are loaded as whole 1 KB pieces of a 32-channel
+// slab (four lanes per token, eight channels each, summed over the quad by
+// DPP); values as whole 1 KB pieces of the channel-major value block (each
+// lane eight tokens of one channel).
+// ---------------------------------------------------------------------------
+constexpr int kHeadWaves = 8;                     // wavefronts per per-head block
+constexpr int kHeadMaxTeams = 512;                // page-table rows a per-head block handles
+
+template <int D, int C>
+struct HeadChunk {
+    static constexpr int KL = (C / 16) * (D / 32); // 16-byte key loads per lane
+    static constexpr int CH = 1024 / (2 * C);      // value channels per 1 KB load
+    static constexpr int LPC = C / 8;              // lanes sharing one value channel
+    static constexpr int VL = D / CH;              // 16-byte value loads per lane
+    uint4 k[KL];
+    uint4 v[VL];
+};
+
+template <int D>
+struct HeadLds {
+    double q64[D];
+    double s[kHeadMaxTeams];                      // scores, then exp(s - m)
+    double c[kHeadMaxTeams];                      // cumulative sums
+    double pts[kHeadMaxTeams];                    // draw points (M < K <= kHeadMaxTeams when drawing)
+    int32_t pt[kHeadMaxTeams];                    // page-table row
+    uint32_t bits[kHeadMaxTeams / 32];
+    int32_t spre[kHeadMaxTeams / 32 + 1];
+    __attribute__((aligned(16))) float qf[D];     // the query in float32, for the token scores
+    float pw[kHeadWaves][2][32];                  // a chunk's probabilities, per wavefront and buffer
+    float mw[kHeadWaves], lw[kHeadWaves];
+    float accw[kHeadWaves][D];
+    double Z;
+};
+
+// One chunk of the head's list: its team, first token, valid tokens and
+// tile offset (uniform over the wavefront).
+struct HeadChunkDesc {
+    int t, tb, n;
+    size_t base;
+};
+
+template <int D, int C, bool FUSED>
+__global__ __launch_bounds__(kHeadWaves * 64, 1) void santa_head_kernel(Params p) {
+    constexpr int NW = kHeadWaves, NTH = NW * 64;
+    using HC = HeadChunk<D, C>;
+    using Pt = sel::Part<bf16_t, D>;
+    constexpr int ROWS = NTH / sel::kParts;      // representative rows per scoring pass
+    constexpr int PASSES = kHeadMaxTeams / ROWS;
+    __shared__ HeadLds<D> lds;
+
+    // Block -> slot ((group, range), head in group): the G heads of one
+    // (group, range) sit on consecutive slots, hence on one XCD.
+    const int S = p.max_splits;
+    const int nreal = p.B * p.Hq * S;
+    const int slot = int(blockIdx.x & 7) * int(gridDim.x >> 3) + int(blockIdx.x >> 3);
+    if (slot >= nreal) return;
+    const int gi = slot % p.G, rest = slot / p.G;
+    const int j = rest % S, grp = rest / S;
+    const int b = grp / p.Hkv, g = grp - b * p.Hkv;
+    const int h = g * p.G + gi, bh = b * p.Hq + h;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // Round trip 1: length, query, page-table row, and (fused) this
+    // thread's part of every representative row it scores, or the head's
+    // bitmap words.
+    const int Lraw = p.seq_lens[b];
+    const bf16_t *qg = static_cast<const bf16_t *>(p.q) + size_t(bh) * D;
+    uint4 qv = make_uint4(0, 0, 0, 0);
+    if (tid < D / 8) qv = ld16(qg + tid * 8);
+    const int32_t ptv = tid < p.P ? p.page_table[size_t(b) * p.P + tid] : 0;
+    const int row0 = tid / sel::kParts, part = tid % sel::kParts;
+    uint4 raw[FUSED ? PASSES : 1][Pt::LOADS];
+    uint32_t bw = 0u;
+    const sel::TailArgs ta{0, p.M, p.scheme, p.seed_lo, p.seed_hi, p.offset, h, b};
+    if constexpr (FUSED) {
+        const bf16_t *reps = static_cast<const bf16_t *>(p.reps) + size_t(b) * p.P * p.Hkv * D;
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int row = row0 + ps * ROWS;
+            if (row < p.P) sel::load_part<bf16_t, D>(reps + (size_t(row) * p.Hkv + g) * D, part, raw[ps]);
+        }
+        // Draw points while the rows are in flight (M < P <= kHeadMaxTeams
+        // whenever they are used).
+        if (p.M < p.P) sel::draw_points(ta, lds.pts, tid, NTH);
+    } else {
+        if (tid < p.words) bw = p.bitmaps[size_t(bh) * p.words + tid];
+    }
+    if (tid < D / 8) {
+        float f[8];
+        unpack(qv, f, bf16_t{});
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lds.q64[tid * 8 + e] = double(f[e]);
+            lds.qf[tid * 8 + e] = f[e];
+        }
+    }
+    if (tid < p.P) lds.pt[tid] = ptv;
+    const int len = clamp_len(Lraw, p.P * p.T);
+    const int K = (len + p.T - 1) / p.T;
+    if constexpr (!FUSED) {
+        if (tid < p.words) lds.bits[tid] = bw;
+    }
+    __syncthreads();
+
+    if constexpr (FUSED) {
+        // Scores (selection.h order; the query part stays in registers).
+        double qp[Pt::N];
+#pragma unroll
+        for (int i = 0; i < Pt::N; ++i) qp[i] = lds.q64[part * Pt::N + i];
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+            if (ps * ROWS >= K) break;                        // uniform
+            const int t = row0 + ps * ROWS;
+            const double sc = sel::row_score(sel::part_dot_raw<bf16_t, D>(raw[ps], qp), p.scale);
+            if (part == 0 && t < K) lds.s[t] = sc;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            sel::TailArgs a = ta;
+            a.K = K;
+            const double Z = sel::head_tail(lds.s, lds.c, lds.bits, lds.pts, a);
+            if (lane == 0) lds.Z = Z;
+        }
+        __syncthreads();
+    }
+
+    // The head's drawn teams in order: popcount prefix of the bitmap words.
+    const int words = (K + 31) >> 5;
+    if (wave == 0) {
+        const int cnt = lane < words ? __popc(lds.bits[lane]) : 0;
+        const int ic = sel::wave_incl_scan(cnt);
+        if (lane < words) lds.spre[lane] = ic - cnt;
+        if (lane == 63) lds.spre[words] = ic;
+    }
+    __syncthreads();
+    const int ndrawn = lds.spre[words];
+    const int cpt = p.T >= 32 ? p.T / 32 : 1;
+    const int total = ndrawn * cpt;
+    const int c0 = int((long long)total * j / S), c1 = int((long long)total * (j + 1) / S);
+    const bool full = p.M >= K;
+    const double Z = FUSED ? lds.Z : 0.0;
+    const bool out_sets = FUSED && p.sampled != nullptr;
+    if (out_sets && j == S - 1)
+        for (int r = ndrawn + tid; r < p.M; r += NTH) {
+            p.sampled[size_t(bh) * p.M + r] = -1;
+            p.inv_pi[size_t(bh) * p.M + r] = 0.0f;
+        }
+
+    const float scale = float(p.scale);
+    const float *lnw_g = p.lnw + size_t(bh) * p.P;
+    const bf16_t *kbase = static_cast<const bf16_t *>(p.k_pages);
+    const bf16_t *vbase = static_cast<const bf16_t *>(p.v_pages);
+
+    // Chunk ci of the list: the (ci / cpt)-th drawn team, piece ci mod cpt.
+    auto describe = [&](int ci) {
+        const int rk = ci / cpt, piece = ci - rk * cpt;
+        int lo = 0, hi = words - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (lds.spre[mid] <= rk) lo = mid; else hi = mid - 1;
+        }
+        uint32_t u = lds.bits[lo];
+        for (int k = rk - lds.spre[lo]; k > 0; --k) u &= u - 1u;
+        HeadChunkDesc d;
+        d.t = lo * 32 + __ffs(u) - 1;
+        d.tb = piece * 32;
+        d.n = min(p.T, len - d.t * p.T);
+        d.base = (size_t(clamp_page(lds.pt[d.t], p.num_pages)) * p.Hkv + g) * size_t(p.T) * D + size_t(d.tb) * D;
+        return d;
+    };
+    auto load = [&](const HeadChunkDesc &d, HC &ck) {
+        const bf16_t *kc = kbase + d.base;
+        const bf16_t *vc = vbase + d.base;
+#pragma unroll
+        for (int kk = 0; kk < HC::KL; ++kk) {
+            const int r = kk / (D / 32), sl = kk % (D / 32);
+            ck.k[kk] = ld16_stream(kc + sl * (C * 32) + (r * 16 + (lane >> 2)) * 32 + (lane & 3) * 8);
+        }
+#pragma unroll
+        for (int vv = 0; vv < HC::VL; ++vv)
+            ck.v[vv] = ld16_stream(vc + (vv * HC::CH + lane / HC::LPC) * C + (lane % HC::LPC) * 8);
+    };
+    // Log weight of the chunk's team: computed here for a fused call (while
+    // the chunk's loads are in flight; the selection kernel computes the same
+    // value), and the team's entry of the sorted set written once, by the
+    // block holding its first chunk.
+    auto weight = [&](int ci, const HeadChunkDesc &d) {
+        if constexpr (FUSED) {
+            const double pi = full ? 1.0 : sel::inclusion(lds.s, lds.c, d.t, Z, p.M, p.scheme);
+            if (out_sets && d.tb == 0 && lane == 0) {
+                const int rk = ci / cpt;
+                p.sampled[size_t(bh) * p.M + rk] = d.t;
+                p.inv_pi[size_t(bh) * p.M + rk] = full ? 1.0f : float(1.0 / pi);
+            }
+            return full ? 0.0f : sel::log_weight(pi);
+        } else {
+            return lnw_g[d.t];
+        }
+    };
+
+    float m = kNegInfF, lsum = 0.0f;
+    float acc[HC::VL];
+#pragma unroll
+    for (int r = 0; r < HC::VL; ++r) acc[r] = 0.0f;
+    // Scores, weighted online softmax and P V for one loaded chunk.
+    auto compute = [&](const HeadChunkDesc &d, float lwt, const HC &ck, int buf) {
+        float sc[C / 16];
+        float cmax = kNegInfF;
+#pragma unroll
+        for (int r = 0; r < C / 16; ++r) {
+            float a = 0.0f;
+#pragma unroll
+            for (int sl = 0; sl < D / 32; ++sl) {
+                // the lane's query slice: channels 32 sl + 8 (lane % 4) + e
+                const float4 q0 = *reinterpret_cast<const float4 *>(&lds.qf[sl * 32 + (lane & 3) * 8]);
+                const float4 q1 = *reinterpret_cast<const float4 *>(&lds.qf[sl * 32 + (lane & 3) * 8 + 4]);
+                const float qs[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                float f[8];
+                unpack(ck.k[r * (D / 32) + sl], f, bf16_t{});
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = fmaf(f[e], qs[e], a);
+            }
+            a += __int_as_float(sel::dpp_i<sel::kQuadXor1, 0xF>(__float_as_int(a), 0));
+            a += __int_as_float(sel::dpp_i<sel::kQuadXor2, 0xF>(__float_as_int(a), 0));
+            const int tok = d.tb + r * 16 + (lane >> 2);
+            sc[r] = tok < d.n ? a * scale + lwt : kNegInfF;
+            cmax = fmaxf(cmax, sc[r]);
+        }
+        cmax = sel::wave_max(cmax);
+        const float mnew = fmaxf(m, cmax);
+        const float corr = (m == kNegInfF) ? 0.0f : __expf(m - mnew);
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < C / 16; ++r) {
+            const float pr = sc[r] == kNegInfF ? 0.0f : __expf(sc[r] - mnew);
+            if ((lane & 3) == 0) {
+                lds.pw[wave][buf][r * 16 + (lane >> 2)] = pr;
+                psum += pr;
+            }
+        }
+        psum = sel::wave_sum(psum);
+        lsum = lsum * corr + psum;
+        m = mnew;
+        __builtin_amdgcn_wave_barrier();
+        // Values: channel vv * CH + lane / LPC, tokens 8 (lane % LPC) + e.
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = lds.pw[wave][buf][(lane % HC::LPC) * 8 + e];
+        const int keep = d.n - (d.tb + (lane % HC::LPC) * 8);      // valid tokens among this lane's 8
+#pragma unroll
+        for (int vv = 0; vv < HC::VL; ++vv) {
+            float f[8];
+            unpack(ck.v[vv], f, bf16_t{});
+            float a = acc[vv] * corr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaf(pe[e], e < keep ? f[e] : 0.0f, a);
+            acc[vv] = a;
+        }
+    };
+
+    // Two chunks in flight per wavefront: both are requested, then computed
+    // in order.
+    for (int ci = c0 + wave; ci < c1; ci += 2 * NW) {
+        const int cj = ci + NW;
+        const bool two = cj < c1;                                   // uniform
+        HC ca, cb;
+        const HeadChunkDesc da = describe(ci);
+        load(da, ca);
+        HeadChunkDesc db = da;
+        if (two) {
+            db = describe(cj);
+            load(db, cb);
+        }
+        const float lwa = weight(ci, da);
+        const float lwb = two ? weight(cj, db) : 0.0f;
+        compute(da, lwa, ca, 0);
+        if (two) compute(db, lwb, cb, 1);
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // Wavefront partials: sum the LPC lanes of each channel, then merge the
+    // wavefronts in order and store the block's partial.
+#pragma unroll
+    for (int vv = 0; vv < HC::VL; ++vv) {
+        float a = acc[vv];
+        a += __int_as_float(sel::dpp_i<sel::kQuadXor1, 0xF>(__float_as_int(a), 0));
+        if (HC::LPC == 4) a += __int_as_float(sel::dpp_i<sel::kQuadXor2, 0xF>(__float_as_int(a), 0));
+        if (lane % HC::LPC == 0) lds.accw[wave][vv * HC::CH + lane / HC::LPC] = a;
+    }
+    if (lane == 0) {
+        lds.mw[wave] = m;
+        lds.lw[wave] = lsum;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float mx = kNegInfF;
+        for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds.mw[w]);
+        const size_t sl = size_t(bh) * p.slots + j;
+        if (mx == kNegInfF) {
+            if (tid == 0) write_empty_partial(p, bh, j);
+        } else {
+            float a = 0.0f, l = 0.0f;
+            for (int w = 0; w < NW; ++w) {
+                const float f = lds.mw[w] == kNegInfF ? 0.0f : expf(lds.mw[w] - mx);
+                a += f * lds.accw[w][tid];
+                l += f * lds.lw[w];
+            }
+            p.part_acc[sl * D + tid] = a;
+            if (tid == 0) reinterpret_cast<float2 *>(p.part_ml)[sl] = make_float2(mx, l);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -898,15 +1328,20 @@ __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
         // every slot's value sum are loaded at once; slots that hold no
         // partial of this call get weight 0 and their values are never used.
         __shared__ float2 ml_s[kFew * SUB];
+        // Every load into registers first (one round trip), then into LDS.
         const int Lraw = p.seq_lens[b];
-        if (!dense && !p.ranked && tid < p.words) hw_s[tid] = p.bitmaps[size_t(bh) * p.words + tid];
-        if (tid < p.max_splits) ml_s[tid] = ml[tid];
+        uint32_t hwv = 0u;
+        if (!dense && !p.ranked && tid < p.words) hwv = p.bitmaps[size_t(bh) * p.words + tid];
+        float2 mlv = make_float2(kNegInfF, 0.0f);
+        if (tid < p.max_splits) mlv = ml[tid];
         float4 x[kFew];
 #pragma unroll
         for (int u = 0; u < kFew; ++u) {
             const int sp = sb + u * SUB;
             x[u] = (sp < p.max_splits) ? pacc[size_t(sp) * Q4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        if (!dense && !p.ranked && tid < p.words) hw_s[tid] = hwv;
+        if (tid < p.max_splits) ml_s[tid] = mlv;
         __syncthreads();
         if (nsp <= p.max_splits) {                // uniform; else the slot count needs the general path
             if (wave == 0) {
@@ -1106,8 +1541,27 @@ santa_status launch_gather(const Params &p, void *stream) {
             if (p.d == 64) hipLaunchKernelGGL((gather_balanced_kernel<64, kModeDense>), grid, dim3(kBlock), 0, st, p);
             else hipLaunchKernelGGL((gather_balanced_kernel<128, kModeDense>), grid, dim3(kBlock), 0, st, p);
         } else {
-            if (p.d == 64) hipLaunchKernelGGL((gather_balanced_kernel<64, kModeSanta>), grid, dim3(kBlock), 0, st, p);
-            else hipLaunchKernelGGL((gather_balanced_kernel<128, kModeSanta>), grid, dim3(kBlock), 0, st, p);
+            if (p.per_head) {
+                // One block per (head, range) slot, rounded up to whole XCD rounds.
+                const int64_t nh = int64_t(p.B) * p.Hq * p.max_splits;
+                const dim3 hgrid(unsigned((nh + 7) / 8 * 8)), hblock(kHeadWaves * 64);
+                const bool c16 = p.T < 32;
+#define SANTA_HEAD_LAUNCH(DD, CC)                                                                               \
+    if (p.fused) hipLaunchKernelGGL((santa_head_kernel<DD, CC, true>), hgrid, hblock, 0, st, p);                \
+    else hipLaunchKernelGGL((santa_head_kernel<DD, CC, false>), hgrid, hblock, 0, st, p);
+                if (p.d == 64) {
+                    if (c16) { SANTA_HEAD_LAUNCH(64, 16) } else { SANTA_HEAD_LAUNCH(64, 32) }
+                } else {
+                    if (c16) { SANTA_HEAD_LAUNCH(128, 16) } else { SANTA_HEAD_LAUNCH(128, 32) }
+                }
+#undef SANTA_HEAD_LAUNCH
+                return launched();
+            }
+            // One block per (group, range) slot, rounded up to whole XCD rounds.
+            const int64_t n = int64_t(p.B) * p.Hkv * p.max_splits;
+            const dim3 sgrid(unsigned((n + 7) / 8 * 8)), block(kSantaWaves * 64);
+            if (p.d == 64) hipLaunchKernelGGL((santa_gather_kernel<64, kSantaWaves>), sgrid, block, 0, st, p);
+            else hipLaunchKernelGGL((santa_gather_kernel<128, kSantaWaves>), sgrid, block, 0, st, p);
         }
     } else if (p.dtype == SANTA_BF16) {
         return SANTA_ERR_UNSUPPORTED;             // bf16 caches always take balanced blocks

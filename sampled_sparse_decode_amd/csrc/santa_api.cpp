@@ -79,9 +79,33 @@ static void balanced_split(Params *p) {
     p->max_splits = int32_t(std::min<int64_t>(p->P, std::max<int64_t>(1, (kBalancedBlocks + groups - 1) / groups)));
 }
 
+// Few query heads per call (bfloat16): one block per (head, range) of the
+// head's own drawn chunks, S ranges per head so that about kBalancedBlocks
+// blocks run. Used when the call has at most kPerHeadMaxHeads (sequence,
+// query head) pairs: the per-head blocks then need only one head's
+// selection each and the launch fills the chip.
+static bool per_head_shape(const Params &p) {
+    return p.dtype == SANTA_BF16 && p.P <= kPerHeadMaxTeams && int64_t(p.B) * p.Hq <= kPerHeadMaxHeads;
+}
+
+static void per_head_split(Params *p) {
+    const int64_t heads = int64_t(p->B) * p->Hq;
+    p->balanced = 1;
+    p->per_head = 1;
+    p->ranked = 1;
+    p->tps = 1;
+    p->spread = 0;
+    p->max_splits = int32_t(std::min<int64_t>(p->P, std::max<int64_t>(1, kBalancedBlocks / heads)));
+}
+
 static void santa_split(Params *p) {
     const int64_t groups = int64_t(p->B) * p->Hkv;
     p->balanced = 0;
+    p->per_head = 0;
+    if (per_head_shape(*p)) {
+        per_head_split(p);
+        return;
+    }
     if (p->dtype == SANTA_BF16) {
         balanced_split(p);
         return;
@@ -147,6 +171,20 @@ static santa_status run_gather_combine(Params &p, void *stream) {
     santa_status st = launch_gather(p, stream);
     if (st != SANTA_OK) return st;
     return launch_combine(p, stream);
+}
+
+// Selection, gather and combine of one decode call on a filled-in Params:
+// with per-head blocks, one gather launch that selects for itself; else the
+// selection kernel first. Either gives the same bits as santa_select_teams
+// followed by santa_attend_selected (same split shape, same arithmetic).
+static santa_status run_decode(Params &p, void *stream) {
+    if (p.per_head) {
+        p.fused = 1;
+        return run_gather_combine(p, stream);
+    }
+    santa_status st = launch_select(p, stream);
+    if (st != SANTA_OK) return st;
+    return run_gather_combine(p, stream);
 }
 
 }  // namespace santa
@@ -269,13 +307,21 @@ santa_status santa_decode_attention_ex(const santa_kv *kv, const void *q, const 
                                        int32_t M, uint64_t seed, uint32_t offset, int32_t scheme,
                                        float *out, float *lse, int32_t *sampled, float *inv_pi,
                                        void *workspace, size_t workspace_bytes, void *stream) {
-    santa_status st = validate_kv(kv);
+    Params p;
+    santa_status st = santa_params(kv, q, M, out, lse, workspace, workspace_bytes, &p);
     if (st != SANTA_OK) return st;
-    if (!q || !reps || !out) return SANTA_ERR_NULL;
-    st = santa_select_teams_ex(kv, q, reps, M, seed, offset, scheme, sampled, inv_pi, workspace, workspace_bytes,
-                               stream);
-    if (st != SANTA_OK) return st;
-    return santa_attend_selected(kv, q, M, out, lse, workspace, workspace_bytes, stream);
+    if (!reps || !out) return SANTA_ERR_NULL;
+    if (scheme != SANTA_DRAW_IID && scheme != SANTA_DRAW_SYSTEMATIC && scheme != SANTA_DRAW_STRATIFIED)
+        return SANTA_ERR_SHAPE;
+    if ((sampled == nullptr) != (inv_pi == nullptr)) return SANTA_ERR_NULL;
+    p.scheme = scheme;
+    p.reps = reps;
+    p.seed_lo = uint32_t(seed & 0xffffffffu);
+    p.seed_hi = uint32_t(seed >> 32);
+    p.offset = offset;
+    p.sampled = sampled;
+    p.inv_pi = inv_pi;
+    return run_decode(p, stream);
 }
 
 santa_status santa_decode_attention_noalloc(const santa_kv *kv, const void *q, const void *reps,
@@ -308,9 +354,7 @@ santa_status santa_decode_attention_noalloc(const santa_kv *kv, const void *q, c
     r.offset = offset;
     r.sampled = sampled;
     r.inv_pi = inv_pi;
-    st = launch_select(r, stream);
-    if (st != SANTA_OK) return st;
-    return run_gather_combine(r, stream);
+    return run_decode(r, stream);
 }
 
 santa_status santa_decode_attention(const santa_kv *kv, const void *q, const void *reps,

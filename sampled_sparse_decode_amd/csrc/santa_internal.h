@@ -14,6 +14,9 @@ constexpr int kMaxTeams = 2048;        // max_pages_per_seq limit (LDS-resident 
 constexpr int kMaxWords = kMaxTeams / 32;
 constexpr int kMaxGroup = 16;          // query heads per KV head
 constexpr int kMaxTeamsPerSplit = 16;
+constexpr int kSantaWaves = 8;         // wavefronts per SANTA++ union-gather block (bfloat16)
+constexpr int kPerHeadMaxTeams = 512;  // per-head gather: page-table rows at most
+constexpr int kPerHeadMaxHeads = 64;   // per-head gather: (sequence, query head) pairs per call at most
 
 enum Mode : int32_t { kModeSanta = 0, kModeDense = 1 };
 
@@ -84,6 +87,8 @@ struct Params {
     int32_t update_teams;       // update mode: teams refreshed per sequence at most
     int32_t rep_kind;           // santa_rep_kind of build_reps launches (seed_lo/hi key the random kind)
     int32_t scheme;             // santa_draw_scheme of select launches
+    int32_t per_head;           // 1 (bf16): blocks per (head, range), each head streaming its own teams
+    int32_t fused;              // per-head blocks select their head's teams themselves (one-launch decode)
 };
 
 constexpr uint32_t kRepKeyXor = 0x52455053u;   // random representatives: key word 0 = seed lo ^ this
