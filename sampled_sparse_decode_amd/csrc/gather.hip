@@ -724,7 +724,7 @@ struct HeadLds {
     int32_t spre[kHeadMaxTeams / 32 + 1];
     __attribute__((aligned(16))) float qf[D];     // the query in float32, for the token scores
     float pw[kHeadWaves][2][32];                  // a chunk's probabilities, per wavefront and buffer
-    float mw[kHeadWaves], lw[kHeadWaves];
+    float mw[kHeadWaves], lw[kHeadWaves];        // per-wavefront maxima (scores, then logits) and sums
     float accw[kHeadWaves][D];
     double Z;
 };
@@ -804,26 +804,34 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void santa_head_kernel(Params p
         double qp[Pt::N];
 #pragma unroll
         for (int i = 0; i < Pt::N; ++i) qp[i] = lds.q64[part * Pt::N + i];
+        float mx = -INFINITY;                                 // largest float32-rounded score of the thread's rows
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             if (ps * ROWS >= K) break;                        // uniform
             const int t = row0 + ps * ROWS;
             const double sc = sel::row_score(sel::part_dot_raw<bf16_t, D>(raw[ps], qp), p.scale);
-            if (part == 0 && t < K) lds.s[t] = sc;
+            if (part == 0 && t < K) {
+                lds.s[t] = sc;
+                mx = fmaxf(mx, float(sc));
+            }
         }
+        mx = sel::wave_max(mx);
+        if (lane == 0) lds.mw[wave] = mx;
         __syncthreads();
-        if (wave == 0) {
+        sel::team_exps(lds.s, K, lds.mw, NW, tid, NTH);
+        __syncthreads();
+    }
+
+    // Wavefront 0: the draws (fused), then the head's drawn teams in order as
+    // the popcount prefix of the bitmap words.
+    const int words = (K + 31) >> 5;
+    if (wave == 0) {
+        if constexpr (FUSED) {
             sel::TailArgs a = ta;
             a.K = K;
             const double Z = sel::head_tail(lds.s, lds.c, lds.bits, lds.pts, a);
             if (lane == 0) lds.Z = Z;
         }
-        __syncthreads();
-    }
-
-    // The head's drawn teams in order: popcount prefix of the bitmap words.
-    const int words = (K + 31) >> 5;
-    if (wave == 0) {
         const int cnt = lane < words ? __popc(lds.bits[lane]) : 0;
         const int ic = sel::wave_incl_scan(cnt);
         if (lane < words) lds.spre[lane] = ic - cnt;
@@ -1344,60 +1352,45 @@ __global__ __launch_bounds__(kCombine) void combine_kernel(Params p) {
         if (tid < p.max_splits) ml_s[tid] = mlv;
         __syncthreads();
         if (nsp <= p.max_splits) {                // uniform; else the slot count needs the general path
-            if (wave == 0) {
-                const int L = clamp_len(Lraw, p.P * p.T);
-                const int K = (L + p.T - 1) / p.T;
-                const int nslots = (K + p.tps - 1) / p.tps;
-                const uint32_t low = (p.tps >= 32) ? 0xffffffffu : ((1u << p.tps) - 1u);
-                float mv[2];
-                bool ok[2];
-    #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int sp = lane + 64 * i;
-                    bool hv = sp < nsp;
-                    if (hv) {
-                        if (p.ranked) {
-                            hv = ml_s[sp].x != kNegInfF;
-                        } else {
-                            hv = sp < nslots;
-                            if (hv && !dense) {
-                                const int t0 = sp * p.tps;
-                                hv = ((hw_s[t0 >> 5] >> (t0 & 31)) & low) != 0u;
-                            }
-                        }
-                    }
-                    ok[i] = hv;
-                    mv[i] = hv ? ml_s[sp].x : kNegInfF;
-                }
-                float mstar = fmaxf(mv[0], mv[1]);
-                for (int off = 32; off > 0; off >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, off, 64));
-                float lpart = 0.0f;
-    #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int sp = lane + 64 * i;
-                    const float f = ok[i] ? expf(mv[i] - mstar) : 0.0f;
-                    if (sp < kFew * SUB) f_s[sp] = f;
-                    if (ok[i]) lpart += f * ml_s[sp].y;
-                }
-                for (int off = 32; off > 0; off >>= 1) lpart += __shfl_xor(lpart, off, 64);
-                if (lane == 0) {
-                    redf[0] = mstar;
-                    redf[1] = lpart;
-                }
+            // Every wavefront forms m* and l itself (DPP, the same order in
+            // each), so no wavefront waits for another before its sums.
+            const int L = clamp_len(Lraw, p.P * p.T);
+            const int K = (L + p.T - 1) / p.T;
+            const int nslots = (K + p.tps - 1) / p.tps;
+            const uint32_t low = (p.tps >= 32) ? 0xffffffffu : ((1u << p.tps) - 1u);
+            auto holds = [&](int sp) {            // slot sp holds a partial of this head
+                if (sp >= nsp) return false;
+                if (p.ranked) return ml_s[sp].x != kNegInfF;
+                if (sp >= nslots) return false;
+                if (dense) return true;
+                const int t0 = sp * p.tps;
+                return ((hw_s[t0 >> 5] >> (t0 & 31)) & low) != 0u;
+            };
+            float mv[2];
+            bool ok[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int sp = lane + 64 * i;
+                ok[i] = holds(sp);
+                mv[i] = ok[i] ? ml_s[sp].x : kNegInfF;
             }
-            __syncthreads();
-            const float mstar = redf[0], l = redf[1];
+            const float mstar = sel::wave_max(fmaxf(mv[0], mv[1]));
             if (mstar == kNegInfF) {                  // no partial: empty sequence
                 for (int c = tid; c < D; c += kCombine) p.out[size_t(bh) * D + c] = 0.0f;
                 if (tid == 0 && p.lse) p.lse[bh] = kNegInfF;
                 return;
             }
+            float lpart = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                if (ok[i]) lpart += expf(mv[i] - mstar) * ml_s[lane + 64 * i].y;
+            const float l = sel::wave_sum(lpart);
             float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    #pragma unroll
+#pragma unroll
             for (int u = 0; u < kFew; ++u) {
                 const int sp = sb + u * SUB;
-                const float f = (sp < p.max_splits) ? f_s[sp] : 0.0f;
-                if (f > 0.0f) {
+                if (sp < p.max_splits && holds(sp)) {
+                    const float f = expf(ml_s[sp].x - mstar);
                     a.x += f * x[u].x; a.y += f * x[u].y; a.z += f * x[u].z; a.w += f * x[u].w;
                 }
             }

@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     __shared__ double pts_s[kMaxTeams];
     __shared__ uint32_t bits_s[kMaxWords];
     __shared__ int32_t pre_s[kMaxWords + 1];
+    __shared__ float wmax_s[kSelThreads / 64];
 
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;
@@ -69,13 +70,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < Pt::N; ++i) qp[i] = q_s[part * Pt::N + i];
 
+    float mx = -INFINITY;                                // largest float32-rounded score of the thread's rows
     if constexpr (UPFRONT) {
 #pragma unroll
         for (int ps = 0; ps < kUpfrontPasses; ++ps) {
             if (ps * kRowsPerPass >= K) break;                  // uniform
             const int t = row0 + ps * kRowsPerPass;
             const double sc = sel::row_score(sel::part_dot_raw<KV, D>(up[ps], qp), p.scale);
-            if (part == 0 && t < K) s_s[t] = sc;
+            if (part == 0 && t < K) {
+                s_s[t] = sc;
+                mx = fmaxf(mx, float(sc));
+            }
         }
     }
     // Scores, one pass of kRowsPerPass rows at a time; the next pass's rows
@@ -89,12 +94,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
             sel::load_part<KV, D>(reps + (size_t(tn < K ? tn : 0) * p.Hkv + g) * D, part, nxt);
         }
         const double sc = sel::row_score(sel::part_dot_raw<KV, D>(raw, qp), p.scale);
-        if (part == 0 && t < K) s_s[t] = sc;
+        if (part == 0 && t < K) {
+            s_s[t] = sc;
+            mx = fmaxf(mx, float(sc));
+        }
         if (more) {
 #pragma unroll
             for (int j = 0; j < Pt::LOADS; ++j) raw[j] = nxt[j];
         }
     }
+    mx = sel::wave_max(mx);
+    if ((tid & 63) == 0) wmax_s[tid >> 6] = mx;
+    __syncthreads();
+    sel::team_exps(s_s, K, wmax_s, kSelThreads / 64, tid, kSelThreads);
     __syncthreads();
     if (tid >= 64) return;
 

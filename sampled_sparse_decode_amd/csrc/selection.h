@@ -259,10 +259,22 @@ __device__ __forceinline__ double inclusion(const double *e, const double *c, in
 // team's terms); the weights reported as 1/pi are float64 quotients.
 __device__ __forceinline__ float log_weight(double pi) { return -logf(float(pi)); }
 
+// Team softmax numerators of one head, by `stride` threads of the block
+// (thread `first` takes teams first, first + stride, ...): m is the largest
+// of the nw per-wavefront maxima in wmax, each the largest float32-rounded
+// score of its wavefront's rows (-inf for none), so m is the float32-rounded
+// maximum score; s_t is overwritten with e_t = exp(s_t - m). The caller
+// makes the block wait before the scan reads them.
+__device__ __forceinline__ void team_exps(double *s, int K, const float *wmax, int nw, int first, int stride) {
+    float mx = -INFINITY;
+    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, wmax[w]);
+    const double m = double(mx);
+    for (int t = first; t < K; t += stride) s[t] = exp(s[t] - m);
+}
+
 // Selection tail of one head, run by one whole wavefront (all 64 lanes call
-// it; no block barrier inside): team softmax, cumulative sums and the draws.
-//   s     [K] float64 scores in LDS; overwritten with e_t = exp(s_t - m),
-//         m the float32-rounded maximum score
+// it; no block barrier inside), after team_exps: cumulative sums and draws.
+//   e     [K] float64 e_t in LDS
 //   c     [K] float64 in LDS: the cumulative sums C_t
 //   bits  [ceil(K/32)] team bitmap in LDS, cleared, then set for drawn teams
 //         (every team when M >= K)
@@ -270,7 +282,7 @@ __device__ __forceinline__ float log_weight(double pi) { return -logf(float(pi))
 // Draw j takes the first team t with pts[j] Z < C_t (binary search); if none
 // qualifies (points below 1 cannot cause that) the last team with mass.
 // Returns Z = C_(K-1) (0 for an empty sequence).
-__device__ __forceinline__ double head_tail(double *s, double *c, uint32_t *bits, const double *pts,
+__device__ __forceinline__ double head_tail(const double *s, double *c, uint32_t *bits, const double *pts,
                                             const TailArgs &a) {
     const int lane = threadIdx.x & 63;
     const int K = a.K;
@@ -278,23 +290,10 @@ __device__ __forceinline__ double head_tail(double *s, double *c, uint32_t *bits
     for (int w = lane; w < words; w += 64) bits[w] = 0u;
     if (K == 0) return 0.0;
 
-    float mx = -INFINITY;
-    for (int t = lane; t < K; t += 64) mx = fmaxf(mx, float(s[t]));
-    const double m = double(wave_max(mx));
     const int per = (K + 63) >> 6;
     const int t0 = min(K, lane * per), t1 = min(K, t0 + per);
     double local = 0.0;
-    for (int t4 = t0; t4 < t1; t4 += 4) {               // four independent exponentials at a time
-        double e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = t4 + i < t1 ? exp(s[t4 + i] - m) : 0.0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (t4 + i < t1) {
-                s[t4 + i] = e[i];
-                local += e[i];
-            }
-    }
+    for (int t = t0; t < t1; ++t) local += s[t];
     const double incl = wave_incl_scan(local);
     double run = incl - local;
     for (int t = t0; t < t1; ++t) {
