@@ -15,8 +15,11 @@ timed loops), with the eager-launch figure reported alongside. The same is timed
 for the gather + combine stage alone (the kernels that move the bytes), whose
 algorithmic bytes give the roofline figure. Two larger configurations (batch
 8 at 32K, batch 4 at 128K) are then measured the same way with fewer steps
-and reported compactly under "at_scale". The CPU oracle is timed on a
-bounded sample of the headline workload at the end.
+and reported compactly under "at_scale". The CPU oracle is timed first (its
+worker processes fork before the GPU is used) on bounded samples of the
+headline workload, on one thread and on every core, each the median of three
+runs. "team_mass" reports how concentrated the team softmax is (the share of
+teams with probability under 1 %, the mean largest probability).
 
 Prints one JSON line.
 """
@@ -137,7 +140,7 @@ def time_graph(fn, R, steps, warmup, torch):
     with torch.cuda.graph(g):
         for i in range(R):
             fn(i)
-    replays = max(1, steps // R)
+    replays = max(1, -(-steps // R))              # whole replays, at least `steps` calls
     for _ in range(max(1, warmup // R)):
         g.replay()
     torch.cuda.synchronize()
@@ -160,7 +163,8 @@ def recorded_traffic(workload_name):
         return None
     rec = json.load(open(path))
     csrc = os.path.join(ROOT, "sampled_sparse_decode_amd", "csrc")
-    src = open(os.path.join(csrc, "gather.hip"), "rb").read() + open(os.path.join(csrc, "device_common.h"), "rb").read()
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("gather.hip", "selection.h", "device_common.h"))
     if hashlib.sha256(src).hexdigest() != rec["kernel_source_sha256"]:
         return None
     return int(rec["read_bytes"] + rec["write_bytes"])
@@ -176,36 +180,102 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the same step,
-    held to one thread (BLAS pools limited to 1): SANTA++ heads, then dense
-    heads, each for about half the budget."""
+_ORACLE = {}
+
+
+def _oracle_state(name, w=None):
+    """Per-process oracle inputs of workload `name` (built once per process;
+    forked workers inherit them)."""
+    if name not in _ORACLE:
+        from oracle import numerics, santa as osanta
+        from sampled_sparse_decode_amd import workloads as W
+        w = w if w is not None else W.FULL_SIZE[name]()
+        kv = osanta.PagedKV(w.dtype, w.k_pages, w.v_pages, w.page_table, w.seq_lens)
+        reps = osanta.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+        heads = [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
+        qs = {bh: numerics.decode(w.q[bh], w.dtype) for bh in heads}
+        _ORACLE[name] = (w, kv, reps, heads, qs)
+    return _ORACLE[name]
+
+
+def _one_thread():
+    """Holds this process's BLAS / OpenMP pools to one thread from here on."""
     from threadpoolctl import threadpool_limits
-    from oracle import numerics, santa as osanta
-    kv = osanta.PagedKV(w.dtype, w.k_pages, w.v_pages, w.page_table, w.seq_lens)
-    heads = [(b, h) for b in range(w.batch) for h in range(w.num_q_heads)]
-    reps = osanta.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
-    qs = {bh: numerics.decode(w.q[bh], w.dtype) for bh in heads}
+    global _LIMIT
+    _LIMIT = threadpool_limits(limits=1)
 
-    def timed(fn):
-        done = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s / 2 and done < len(heads) * 4:
-            fn(done)
-            done += 1
-        return (time.perf_counter() - t0) / done * len(heads) * 1e6, done
 
-    with threadpool_limits(limits=1):
-        santa_us, n_santa = timed(lambda i: osanta.santa_head(
-            kv, qs[heads[i % len(heads)]], reps, heads[i % len(heads)][0], heads[i % len(heads)][1],
-            w.num_q_heads, w.M, w.seed, i // len(heads)))
-        dense_us, n_dense = timed(lambda i: osanta.dense_head(
-            kv, qs[heads[i % len(heads)]], heads[i % len(heads)][0], heads[i % len(heads)][1], w.num_q_heads))
-    return {"value": round(santa_us, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "dense_value": round(dense_us, 1), "cpu": cpu_model(),
-            "sample": f"{n_santa} SANTA++ and {n_dense} dense (sequence, query head) evaluations of {w.name} "
-                      f"({len(heads)} per layer), float64 Python/numpy oracle on one thread, "
-                      f"representatives precomputed; scaled to one layer"}
+def _oracle_eval(task):
+    """One oracle evaluation (kind, workload, index)."""
+    from oracle import santa as osanta
+    kind, name, i = task
+    w, kv, reps, heads, qs = _oracle_state(name)
+    b, h = heads[i % len(heads)]
+    if kind == "santa":
+        osanta.santa_head(kv, qs[(b, h)], reps, b, h, w.num_q_heads, w.M, w.seed, i // len(heads))
+    else:
+        osanta.dense_head(kv, qs[(b, h)], b, h, w.num_q_heads)
+
+
+def cpu_baseline(w, name, budget_s):
+    """The CPU oracle, as it stands, on bounded samples of the same step:
+    SANTA++ and dense (sequence, query head) evaluations, on one thread and on
+    every core this process may use (capped at 16, one single-threaded worker
+    process each, started before the GPU is touched), each the median of three
+    timed runs, scaled to one layer. A one-thread run covers one layer; an
+    all-cores run covers one layer per worker. A kind's repeats stop early
+    once it has taken half of `budget_s` seconds."""
+    import multiprocessing as mp
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    heads_per_layer = w.batch * w.num_q_heads
+    _oracle_state(name, w)
+    from threadpoolctl import threadpool_limits
+    runs = {}
+    with threadpool_limits(limits=1), mp.get_context("fork").Pool(cores, initializer=_one_thread) as pool:
+        pool.map(_oracle_eval, [("santa", name, i) for i in range(cores)], chunksize=1)   # warm every worker
+        _oracle_eval(("santa", name, 0))
+        for kind in ("santa", "dense"):
+            t_begin = time.perf_counter()
+            one, many = [], []
+            for rep in range(3):
+                n1 = heads_per_layer
+                t0 = time.perf_counter()
+                for i in range(n1):
+                    _oracle_eval((kind, name, rep * n1 + i))
+                one.append((time.perf_counter() - t0) / n1 * heads_per_layer * 1e6)
+                nm = heads_per_layer * cores
+                t0 = time.perf_counter()
+                pool.map(_oracle_eval, [(kind, name, rep * nm + i) for i in range(nm)], chunksize=1)
+                many.append((time.perf_counter() - t0) / nm * heads_per_layer * 1e6)
+                if time.perf_counter() - t_begin > budget_s / 2:
+                    break
+            runs[kind] = (sorted(one)[len(one) // 2], sorted(many)[len(many) // 2], len(one))
+    santa1, santaN, n = runs["santa"]
+    dense1, denseN, _ = runs["dense"]
+    return {"value": round(santaN, 1), "unit": "us/layer", "cores": cores, "kind": "oracle",
+            "value_1thread": round(santa1, 1), "dense_value": round(denseN, 1), "dense_value_1thread": round(dense1, 1),
+            "cpu": cpu_model(),
+            "sample": f"{name}: per kind, the median of {n} runs of one layer ({heads_per_layer} (sequence, query "
+                      f"head) evaluations) on one thread and of {cores} layers on {cores} single-threaded "
+                      f"processes; float64 Python/numpy oracle, representatives precomputed; scaled to one layer"}
+
+
+def team_mass(w, q, reps, torch):
+    """How concentrated the team softmax is: over (sequence, query head), the
+    share of a sequence's teams whose probability p_t = softmax_t(q . rep_t /
+    sqrt(d)) is below 1 %, and the mean largest p_t (float32, from the
+    representatives the decode call uses)."""
+    B, Hq, d = q.shape
+    G = Hq // reps.shape[2]
+    qf = q.float().reshape(B, reps.shape[2], G, d)
+    rt = reps.float().permute(0, 2, 3, 1).contiguous()                          # [B, Hkv, d, P]
+    s = torch.matmul(qf.contiguous(), rt) / math.sqrt(d)                        # [B, Hkv, G, P]
+    K = torch.as_tensor([-(-int(L) // w.page_size) for L in w.seq_lens], device=q.device)
+    valid = torch.arange(reps.shape[1], device=q.device)[None, :] < K[:, None]  # [B, P]
+    s = s.masked_fill(~valid[:, None, None, :], float("-inf"))
+    pt = torch.softmax(s, dim=-1)
+    low = ((pt < 0.01) & valid[:, None, None, :]).sum(-1).float() / K.clamp(min=1)[:, None, None].float()
+    return {"share_p_below_1pct": round(low.mean().item(), 4), "mean_max_p": round(pt.amax(-1).mean().item(), 4)}
 
 
 def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
@@ -230,6 +300,7 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
     _, _, sampled, _ = S.santa_decode_attention(kv0, q, reps[0], M, w.seed, w.offset, wss[0], return_sets=True)
     torch.cuda.synchronize()
     ab = algorithmic_bytes(w, union_stats(w, sampled.cpu().numpy()))
+    r_mass = team_mass(w, q, reps[0], torch)
 
     def santa_step(i):
         j = i % R
@@ -244,7 +315,7 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
         S.santa_attend_selected(cache[j], q, M, wss[j], out, lse)
 
     # Eager (stream) timings, then HIP-graph replay timings of the same calls.
-    r = dict(R=R, ab=ab)
+    r = dict(R=R, ab=ab, mass=r_mass)
     r["santa_stream_us"] = time_stream(santa_step, steps, warmup, torch)
     r["dense_stream_us"] = time_stream(dense_step, steps, warmup, torch)
     r["santa_us"], r["timed_steps"] = median_graph(santa_step, R, steps, warmup, torch)
@@ -395,8 +466,10 @@ def main():
     import torch
     from sampled_sparse_decode_amd import santa as S, workloads as W
 
-    torch.cuda.set_device(torch.device("cuda:0"))
     w = W.FULL_SIZE[args.workload]()
+    # The CPU oracle first: its worker processes fork before the GPU is used.
+    cpu = None if args.no_cpu else cpu_baseline(w, args.workload, args.cpu_seconds)
+    torch.cuda.set_device(torch.device("cuda:0"))
     r = measure(w, args.steps, args.warmup, args.layers, torch, S, args.calibrate, not args.no_extras)
     ab = r["ab"]
     santa_us, dense_us, attend_us = r["santa_us"], r["dense_us"], r["attend_us"]
@@ -429,6 +502,7 @@ def main():
                   "bytes": ab["dense"]},
         "speedup_vs_dense": round(dense_us / santa_us, 3),
         "kv_read_fraction": {"per_query_head": round(ab["frac_head"], 4), "hbm": round(ab["frac_hbm"], 4)},
+        "team_mass": r["mass"],
         "update_reps_us": round(r["update_reps_us"], 3),
         "build_reps_us": {k: round(v, 2) for k, v in r["build_reps_us"].items()},
         "draw_schemes": r["schemes"],
@@ -451,7 +525,7 @@ def main():
                        "attend_us": round(rs["attend_us"], 2),
                        "attend_frac_of_peak": round(gbps(a["attend"], rs["attend_us"]) / HBM_PEAK_GBPS, 4),
                        "dense_frac_of_peak": round(gbps(a["dense"], rs["dense_us"]) / HBM_PEAK_GBPS, 4),
-                       "kv_read_fraction_hbm": round(a["frac_hbm"], 4),
+                       "kv_read_fraction_hbm": round(a["frac_hbm"], 4), "team_mass": rs["mass"],
                        "build_reps_us": {k: round(v, 2) for k, v in rs["build_reps_us"].items()},
                        "draw_schemes": rs["schemes"],
                        "hashed_teams": rs["hashed"], "kmeans_teams": rs["kmeans"]}
@@ -459,8 +533,8 @@ def main():
         torch.cuda.empty_cache()
     if scale:
         result["at_scale"] = scale
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
