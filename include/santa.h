@@ -158,6 +158,32 @@ typedef enum santa_rep_kind {
 santa_status santa_update_reps(const santa_kv *kv, void *reps, const int32_t *prev_seq_lens,
                                int32_t max_new_tokens, void *stream);
 
+/* Appended tokens into the cache ([EXP] section 三 step 2: the cache grows
+ * by a token per decode step, and the team holding it must stay consistent
+ * with its representative). For each sequence b, the tokens at positions
+ * prev_seq_lens[b] .. kv->seq_lens[b] - 1 are copied, exactly, from row
+ * i = position - prev_seq_lens[b] of k_new / v_new into page
+ * page_table[b][position / T], token position mod T, every channel at its
+ * tile-order offset (the layout santa_pack_pages writes). A serving step is
+ * then: write the new lengths into kv->seq_lens, santa_append_kv,
+ * santa_update_reps with the old lengths, decode.
+ *   kv              kv->seq_lens holds the new lengths; the pages are written
+ *                   through kv->k_pages / kv->v_pages
+ *   prev_seq_lens   [B] int32, device: lengths before the append; a sequence
+ *                   whose length did not grow writes nothing
+ *   k_new, v_new    [B][max_new_tokens][Hkv][d] dtype, device: row i of
+ *                   sequence b is its i-th new token; rows at or beyond the
+ *                   sequence's count are not read
+ *   max_new_tokens  host bound on the tokens appended to any one sequence
+ *                   (>= 0; 0 enqueues nothing); more new tokens than this in
+ *                   device lengths are not written
+ * Positions at or beyond T * max_pages_per_seq, and page ids outside
+ * [0, num_pages), are skipped (nothing is written for them). Returns
+ * SANTA_ERR_NULL for a missing pointer, SANTA_ERR_SHAPE for a negative
+ * max_new_tokens or B * max_new_tokens * Hkv * d >= 2^31. */
+santa_status santa_append_kv(const santa_kv *kv, const int32_t *prev_seq_lens, const void *k_new,
+                             const void *v_new, int32_t max_new_tokens, void *stream);
+
 /* Representatives of another kind ([EXP] section 三 step 2: mean, medoid or
  * random member), built for every team or refreshed after an append.
  *   kind            SANTA_REP_MEAN: exactly santa_build_reps (or, with

@@ -228,6 +228,21 @@ santa_status santa_update_reps(const santa_kv *kv, void *reps, const int32_t *pr
     return launch_build_reps(p, stream);
 }
 
+santa_status santa_append_kv(const santa_kv *kv, const int32_t *prev_seq_lens, const void *k_new,
+                             const void *v_new, int32_t max_new_tokens, void *stream) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!prev_seq_lens || !k_new || !v_new) return SANTA_ERR_NULL;
+    if (max_new_tokens < 0) return SANTA_ERR_SHAPE;
+    if (max_new_tokens == 0) return SANTA_OK;
+    const int64_t threads = int64_t(kv->batch) * max_new_tokens * kv->num_kv_heads * kv->head_dim;
+    if (threads >= (int64_t(1) << 31)) return SANTA_ERR_SHAPE;     // one thread per element, 32-bit grid
+    AppendParams ap{k_new, v_new, const_cast<void *>(kv->k_pages), const_cast<void *>(kv->v_pages),
+                    kv->page_table, kv->seq_lens, prev_seq_lens, kv->num_pages, kv->dtype, kv->batch,
+                    kv->max_pages_per_seq, kv->num_kv_heads, kv->page_size, kv->head_dim, max_new_tokens};
+    return launch_append_kv(ap, stream);
+}
+
 santa_status santa_build_reps_ex(const santa_kv *kv, void *reps, int32_t kind, uint64_t seed,
                                  const int32_t *prev_seq_lens, int32_t max_new_tokens, void *stream) {
     santa_status st = validate_kv(kv);

@@ -94,6 +94,19 @@ struct Params {
 constexpr uint32_t kRepKeyXor = 0x52455053u;   // random representatives: key word 0 = seed lo ^ this
 
 // santa_pack_pages arguments.
+// Arguments of the append kernel (santa_append_kv).
+struct AppendParams {
+    const void *k_new;
+    const void *v_new;
+    void *k_pages;
+    void *v_pages;
+    const int32_t *page_table;
+    const int32_t *seq_lens;     // new lengths
+    const int32_t *prev_lens;    // lengths before the append
+    int64_t num_pages;
+    int32_t dtype, B, P, Hkv, T, d, max_new;
+};
+
 struct PackParams {
     const void *k_src;
     const void *v_src;
@@ -138,6 +151,7 @@ santa_status launch_given(const Params &p, void *stream);
 santa_status launch_gather(const Params &p, void *stream);
 santa_status launch_combine(const Params &p, void *stream);
 santa_status launch_pack_pages(const PackParams &pp, void *stream);
+santa_status launch_append_kv(const AppendParams &ap, void *stream);
 santa_status launch_pack_hashed(const ClusterParams &c, void *stream);
 santa_status launch_pack_kmeans(const ClusterParams &c, int32_t iters, void *stream);
 

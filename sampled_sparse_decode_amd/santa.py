@@ -22,6 +22,7 @@ EXPORTED = (
     "santa_workspace_size",
     "santa_build_reps",
     "santa_update_reps",
+    "santa_append_kv",
     "santa_build_reps_ex",
     "santa_decode_attention",
     "santa_decode_attention_ex",
@@ -84,6 +85,7 @@ def load():
         "santa_workspace_size": (i32, [kvp, i32, ctypes.POINTER(sz)]),
         "santa_build_reps": (i32, [kvp, P, P]),
         "santa_update_reps": (i32, [kvp, P, P, i32, P]),
+        "santa_append_kv": (i32, [kvp, P, P, P, i32, P]),
         "santa_build_reps_ex": (i32, [kvp, P, i32, u64, P, i32, P]),
         "santa_decode_attention": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P, sz, P]),
         "santa_decode_attention_ex": (i32, [kvp, P, P, i32, u64, u32, i32, P, P, P, P, P, sz, P]),
@@ -335,6 +337,25 @@ def santa_update_reps(kv, reps, prev_seq_lens, max_new_tokens):
     _check("santa_update_reps", load().santa_update_reps(ctypes.byref(d), _ptr(reps), _ptr(prev_seq_lens),
                                                         int(max_new_tokens), _stream()))
     return reps
+
+
+def santa_append_kv(kv, prev_seq_lens, k_new, v_new):
+    """Write appended tokens into the cache's tile layout: for each sequence
+    b, the tokens at positions prev_seq_lens[b] .. kv.seq_lens[b] - 1 come
+    from rows 0, 1, ... of k_new[b] / v_new[b] ([B][max_new][Hkv][d], the
+    cache dtype). kv.seq_lens must already hold the new lengths."""
+    if prev_seq_lens.dtype != torch.int32 or tuple(prev_seq_lens.shape) != (kv.batch,):
+        raise ValueError("prev_seq_lens must be an int32 [B] tensor")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if (t.dim() != 4 or t.shape[0] != kv.batch or t.shape[2] != kv.num_kv_heads or t.shape[3] != kv.head_dim
+                or t.dtype != kv.dtype or t.device != kv.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [B, max_new, Hkv, d] tensor of the cache's dtype "
+                             f"on its device")
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must have the same shape")
+    d = kv.desc()
+    _check("santa_append_kv", load().santa_append_kv(ctypes.byref(d), _ptr(prev_seq_lens), _ptr(k_new),
+                                                    _ptr(v_new), int(k_new.shape[1]), _stream()))
 
 
 REP_MEAN, REP_MEDOID, REP_RANDOM = 0, 1, 2

@@ -185,6 +185,19 @@ def test_update_reps_validation(lib):
     assert lib.santa_update_reps(ctypes.byref(kv(page_size=48)), F, F, 1, None) == UNSUP
 
 
+def test_append_kv_validation(lib):
+    """santa_append_kv checks its arguments on the host; 0 new tokens enqueues nothing."""
+    k = kv()
+    F = ctypes.c_void_p(FAKE)
+    assert lib.santa_append_kv(ctypes.byref(k), None, F, F, 1, None) == NULL
+    assert lib.santa_append_kv(ctypes.byref(k), F, None, F, 1, None) == NULL
+    assert lib.santa_append_kv(ctypes.byref(k), F, F, None, 1, None) == NULL
+    assert lib.santa_append_kv(ctypes.byref(k), F, F, F, -1, None) == SHAPE
+    assert lib.santa_append_kv(ctypes.byref(k), F, F, F, 0, None) == OK
+    assert lib.santa_append_kv(ctypes.byref(kv(page_size=48)), F, F, F, 1, None) == UNSUP
+    assert lib.santa_append_kv(ctypes.byref(kv(batch=65535)), F, F, F, 1 << 30, None) == SHAPE
+
+
 def test_build_reps_ex_validation(lib):
     """santa_build_reps_ex: unknown kinds and bad update bounds are rejected
     on the host; an update with 0 new tokens enqueues nothing."""
@@ -321,3 +334,11 @@ def test_binding_rejects_mismatched_buffers():
                              torch.zeros((B, Hkv * G, 5), dtype=torch.int32), torch.zeros((B, Hkv * G, 5)))
     with pytest.raises(ValueError):
         S.dense_decode_attention(kv, q, torch.zeros(16, dtype=torch.float32))
+    prev = torch.zeros((B,), dtype=torch.int32)
+    new = torch.zeros((B, 1, Hkv, d), dtype=torch.bfloat16)
+    for kb, vb in ((new.float(), new.float()), (new[:, :, :1], new[:, :, :1]), (new, new[:1]),
+                   (torch.zeros((B, 2, Hkv, 2 * d), dtype=torch.bfloat16)[..., ::2], new)):
+        with pytest.raises(ValueError):
+            S.santa_append_kv(kv, prev, kb, vb)
+    with pytest.raises(ValueError):
+        S.santa_append_kv(kv, prev.long(), new, new)
