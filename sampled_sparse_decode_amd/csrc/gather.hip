@@ -722,11 +722,12 @@ struct HeadLds {
     int32_t pt[kHeadMaxTeams];                    // page-table row
     uint32_t bits[kHeadMaxTeams / 32];
     int32_t spre[kHeadMaxTeams / 32 + 1];
+    float lnw[kHeadMaxTeams];                     // log weight of each drawn team, by team (fused)
+    float ipi[kHeadMaxTeams];                     // 1 / pi of each drawn team, by team (fused, sets requested)
     __attribute__((aligned(16))) float qf[D];     // the query in float32, for the token scores
     float pw[kHeadWaves][2][32];                  // a chunk's probabilities, per wavefront and buffer
     float mw[kHeadWaves], lw[kHeadWaves];        // per-wavefront maxima (scores, then logits) and sums
     float accw[kHeadWaves][D];
-    double Z;
 };
 
 // One chunk of the head's list: its team, first token, valid tokens and
@@ -822,15 +823,31 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void santa_head_kernel(Params p
         __syncthreads();
     }
 
-    // Wavefront 0: the draws (fused), then the head's drawn teams in order as
-    // the popcount prefix of the bitmap words.
+    // The head's drawn teams in order: rank rk is the team of the rk-th set
+    // bit, found from the popcount prefix spre of the bitmap words.
     const int words = (K + 31) >> 5;
+    const int cpt = p.T >= 32 ? p.T / 32 : 1;             // chunks per team
+    const bool full = p.M >= K;
+    auto team_of = [&](int rk) {
+        int lo = 0, hi = words - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (lds.spre[mid] <= rk) lo = mid; else hi = mid - 1;
+        }
+        uint32_t u = lds.bits[lo];
+        for (int k = rk - lds.spre[lo]; k > 0; --k) u &= u - 1u;
+        return lo * 32 + __ffs(u) - 1;
+    };
+    // This block's chunks [c0, c1) of the head's ndrawn * cpt, and the ranks
+    // of their teams.
+    const bool out_sets = FUSED && p.sampled != nullptr;
+    // Wavefront 0: the draws (fused; each drawing lane also stores its
+    // team's weights), then the popcount prefix.
     if (wave == 0) {
         if constexpr (FUSED) {
             sel::TailArgs a = ta;
             a.K = K;
-            const double Z = sel::head_tail(lds.s, lds.c, lds.bits, lds.pts, a);
-            if (lane == 0) lds.Z = Z;
+            sel::head_tail(lds.s, lds.c, lds.bits, lds.pts, a, lds.lnw, out_sets ? lds.ipi : nullptr);
         }
         const int cnt = lane < words ? __popc(lds.bits[lane]) : 0;
         const int ic = sel::wave_incl_scan(cnt);
@@ -838,13 +855,11 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void santa_head_kernel(Params p
         if (lane == 63) lds.spre[words] = ic;
     }
     __syncthreads();
+    // This block's chunks [c0, c1) of the head's ndrawn * cpt (total * S <
+    // 2^31: ndrawn <= 512, cpt <= 8, S <= 512).
     const int ndrawn = lds.spre[words];
-    const int cpt = p.T >= 32 ? p.T / 32 : 1;
     const int total = ndrawn * cpt;
-    const int c0 = int((long long)total * j / S), c1 = int((long long)total * (j + 1) / S);
-    const bool full = p.M >= K;
-    const double Z = FUSED ? lds.Z : 0.0;
-    const bool out_sets = FUSED && p.sampled != nullptr;
+    const int c0 = total * j / S, c1 = total * (j + 1) / S;
     if (out_sets && j == S - 1)
         for (int r = ndrawn + tid; r < p.M; r += NTH) {
             p.sampled[size_t(bh) * p.M + r] = -1;
@@ -859,15 +874,8 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void santa_head_kernel(Params p
     // Chunk ci of the list: the (ci / cpt)-th drawn team, piece ci mod cpt.
     auto describe = [&](int ci) {
         const int rk = ci / cpt, piece = ci - rk * cpt;
-        int lo = 0, hi = words - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (lds.spre[mid] <= rk) lo = mid; else hi = mid - 1;
-        }
-        uint32_t u = lds.bits[lo];
-        for (int k = rk - lds.spre[lo]; k > 0; --k) u &= u - 1u;
         HeadChunkDesc d;
-        d.t = lo * 32 + __ffs(u) - 1;
+        d.t = team_of(rk);
         d.tb = piece * 32;
         d.n = min(p.T, len - d.t * p.T);
         d.base = (size_t(clamp_page(lds.pt[d.t], p.num_pages)) * p.Hkv + g) * size_t(p.T) * D + size_t(d.tb) * D;
@@ -885,19 +893,16 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void santa_head_kernel(Params p
         for (int vv = 0; vv < HC::VL; ++vv)
             ck.v[vv] = ld16_stream(vc + (vv * HC::CH + lane / HC::LPC) * C + (lane % HC::LPC) * 8);
     };
-    // Log weight of the chunk's team: computed here for a fused call (while
-    // the chunk's loads are in flight; the selection kernel computes the same
-    // value), and the team's entry of the sorted set written once, by the
-    // block holding its first chunk.
+    // Log weight of the chunk's team (the selection kernel computes the same
+    // value for the unfused call); a fused call also writes the team's entry
+    // of the sorted set, from the block holding the team's first chunk.
     auto weight = [&](int ci, const HeadChunkDesc &d) {
         if constexpr (FUSED) {
-            const double pi = full ? 1.0 : sel::inclusion(lds.s, lds.c, d.t, Z, p.M, p.scheme);
             if (out_sets && d.tb == 0 && lane == 0) {
-                const int rk = ci / cpt;
-                p.sampled[size_t(bh) * p.M + rk] = d.t;
-                p.inv_pi[size_t(bh) * p.M + rk] = full ? 1.0f : float(1.0 / pi);
+                p.sampled[size_t(bh) * p.M + ci / cpt] = d.t;
+                p.inv_pi[size_t(bh) * p.M + ci / cpt] = full ? 1.0f : lds.ipi[d.t];
             }
-            return full ? 0.0f : sel::log_weight(pi);
+            return full ? 0.0f : lds.lnw[d.t];
         } else {
             return lnw_g[d.t];
         }

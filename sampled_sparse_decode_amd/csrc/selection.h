@@ -279,11 +279,14 @@ __device__ __forceinline__ void team_exps(double *s, int K, const float *wmax, i
 //   bits  [ceil(K/32)] team bitmap in LDS, cleared, then set for drawn teams
 //         (every team when M >= K)
 //   pts   [M] draw points (draw_points), read when M < K
+//   lnw_t, ipi_t  optional [K] LDS arrays by team: the lane that draws team
+//         t stores log_weight(pi_t) and float(1 / pi_t) there (several draws
+//         of one team store the same values); untouched when M >= K
 // Draw j takes the first team t with pts[j] Z < C_t (binary search); if none
 // qualifies (points below 1 cannot cause that) the last team with mass.
 // Returns Z = C_(K-1) (0 for an empty sequence).
 __device__ __forceinline__ double head_tail(const double *s, double *c, uint32_t *bits, const double *pts,
-                                            const TailArgs &a) {
+                                            const TailArgs &a, float *lnw_t = nullptr, float *ipi_t = nullptr) {
     const int lane = threadIdx.x & 63;
     const int K = a.K;
     const int words = (K + 31) >> 5;
@@ -322,6 +325,11 @@ __device__ __forceinline__ double head_tail(const double *s, double *c, uint32_t
                 while (t > 0 && !(s[t] > 0.0)) --t;
             }
             atomicOr(&bits[t >> 5], 1u << (t & 31));
+            if (lnw_t) {
+                const double pi = inclusion(s, c, t, Z, a.M, a.scheme);
+                lnw_t[t] = log_weight(pi);
+                if (ipi_t) ipi_t[t] = float(1.0 / pi);
+            }
         }
     }
     __builtin_amdgcn_wave_barrier();
