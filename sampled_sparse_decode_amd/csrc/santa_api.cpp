@@ -574,6 +574,6 @@ const char *santa_status_string(int32_t status) {
     }
 }
 
-int32_t santa_version(void) { return 240; }
+int32_t santa_version(void) { return 250; }
 
 }  // extern "C"

@@ -93,7 +93,6 @@ struct Params {
 
 constexpr uint32_t kRepKeyXor = 0x52455053u;   // random representatives: key word 0 = seed lo ^ this
 
-// santa_pack_pages arguments.
 // Arguments of the append kernel (santa_append_kv).
 struct AppendParams {
     const void *k_new;
@@ -107,6 +106,7 @@ struct AppendParams {
     int32_t dtype, B, P, Hkv, T, d, max_new;
 };
 
+// santa_pack_pages arguments.
 struct PackParams {
     const void *k_src;
     const void *v_src;

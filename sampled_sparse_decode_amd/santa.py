@@ -77,7 +77,13 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m sampled_sparse_decode_amd.build")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = declare_signatures(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare_signatures(lib):
+    """Set the argument and result types of every exported entry point on a
+    ctypes handle of a libsanta build; returns it."""
     P = ctypes.c_void_p
     kvp = ctypes.POINTER(santa_kv)
     i32, u32, u64, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t
@@ -106,7 +112,6 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
 
 

@@ -24,8 +24,16 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
 
+# SANTA_TEST_LIB names another build of the same C ABI to check (the
+# host-only sanitizer build of tests/test_host_sanitized.py); default: the
+# library the binding loads.
+TEST_LIB = os.environ.get("SANTA_TEST_LIB")
+
+
 @pytest.fixture(scope="module")
 def lib():
+    if TEST_LIB:
+        return S.declare_signatures(ctypes.CDLL(TEST_LIB))
     if not os.path.exists(S.LIB_PATH):
         pytest.skip("libsanta.so not built")
     return S.load()
