@@ -55,7 +55,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.santa_version() == 240
+    assert lib.santa_version() == 250
     for code in range(6):
         assert S.santa_status_string(code)
     assert S.santa_status_string(99) == "unknown status"
