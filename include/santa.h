@@ -8,13 +8,13 @@
  *         section 三 (core method) and its sub-sections 3.1-3.2.
  *
  * What the library computes, for one decode step of one attention layer
- * ([ABS]; [EXP] section 三): every new query (one per sequence and query head)
- * scores one representative key per team of cached tokens, turns the scores
- * into a team-level softmax p, draws M teams from p, computes exact attention
- * only inside the drawn teams, and weights each drawn team by the inverse of
- * its inclusion probability pi = 1 - (1 - p)^M, which makes the result an
- * estimate of attention over the whole cache. A dense decode over every
- * cached token, built from the same kernels, is exported as the baseline.
+ * ([ABS]; [EXP] section 三): for every new query (one per sequence and query
+ * head), a dot product with each team's summary key and a softmax give team
+ * probabilities p; M draws from p pick the teams whose tokens are read and
+ * scored exactly; a drawn team's terms count 1/pi times, pi = 1 - (1 - p)^M
+ * its chance of being drawn, so the weighted sums stand in, without bias, for
+ * the sums over every cached token. A dense decode over every cached token,
+ * built from the same kernels, is exported as the baseline.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -125,8 +125,8 @@ santa_status santa_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes);
 /* Representative keys: reps[b][t][g][:] = the mean of the keys of team t of
  * sequence b for KV head g, rounded once (to nearest, ties to even) to the
  * cache dtype. [EXP] section 三 step 2 (one representative key per team:
- * mean, medoid or random are listed; the mean is used); [ABS] (the query
- * scores one representative from each team). The mean is the float64 sum of
+ * mean, medoid or random are listed; the mean is used); [ABS] (selection
+ * reads these summary keys, not the cache). The mean is the float64 sum of
  * the n valid keys divided by n (n < T only for a sequence's last team).
  *   reps  [B][max_pages_per_seq][Hkv][d] dtype, indexed by logical team so
  *         that selection reads it without a page-table lookup; written for

@@ -3,13 +3,12 @@
 TEST INFRASTRUCTURE (see the package docstring): the plain, slow reference the
 HIP path is compared with. It shares no code with that path.
 
-What the method computes ([ABS]; [EXP] section 三 "核心方法"): cached keys are
-grouped into teams; the new query scores one representative key per team; a
-softmax over those scores gives team probabilities p; teams are sampled with
-those probabilities; exact attention scores are computed only inside the
-sampled teams; each team's contribution is re-weighted by the inverse of its
-inclusion probability, which makes the result an importance-sampling estimate
-of attention over the whole cache.
+What the method computes ([ABS]; [EXP] section 三 "核心方法"): the cache is
+partitioned into teams, each summarised by one key; the query's dot products
+with those keys, through a softmax, give each team a probability p; M teams
+are drawn from p; only the drawn teams' tokens get exact scores; a drawn
+team's terms count 1/pi times, pi the chance the team was drawn at all, so
+the sums over drawn teams are unbiased for the sums over every token.
 
 Readings taken where the pages leave a step open (each repeated where used):
   R1  teams are contiguous runs of T tokens, one team per KV page; the last
@@ -20,10 +19,10 @@ Readings taken where the pages leave a step open (each repeated where used):
   R3  team scores and token scores carry the usual 1/sqrt(d) factor.
   R4  "sample M teams" = M independent draws with replacement by inverse CDF,
       then duplicates removed; inclusion probability pi = 1 - (1 - p)^M and the
-      weight is 1/pi ([ABS]: inverse of the inclusion probability; [EXP]
-      step 5 writes 1/p_i, which the abstract overrides).
-  R5  the estimate of the attention output is the ratio of the re-weighted
-      numerator sum to the re-weighted denominator sum (both sums are
+      weight is 1/pi ([ABS] weights a drawn team by 1/pi; [EXP] step 5
+      writes 1/p_i, which the abstract overrides).
+  R5  the estimate of the attention output is the ratio of the weighted
+      numerator sum to the weighted denominator sum (both sums are
       unbiased; the ratio is consistent).
   R6  if M >= number of teams, every team is read and pi = 1 (full coverage).
   R7  draws are independent per query head; a KV head's G query heads share
@@ -129,8 +128,8 @@ def build_reps(k_pages, page_table, seq_lens, page_size, dtype, seqs=None):
     """Mean key of every team, rounded once to the KV type.
 
     [EXP] section 三 step 2: one representative key per team (mean, medoid or
-    random are listed); [ABS]: the query scores one representative from each
-    team. Reading R2: the mean, as math.fsum(column) / n (exact sum, one
+    random are listed); [ABS]: team selection looks only at these summary
+    keys. Reading R2: the mean, as math.fsum(column) / n (exact sum, one
     correctly rounded divide), then one round-to-nearest-even into the KV type.
 
     Returns a float64 array [B][max_pages][Hkv][d] indexed by logical team;
@@ -463,9 +462,9 @@ def inclusion_probability_scheme(scheme, t, C, Z, p, M):
 def inclusion_probability(p, M):
     """pi = 1 - (1 - p)^M, computed as -expm1(M * log1p(-p)) (R4).
 
-    [ABS]: each sampled team is re-weighted by the inverse of its inclusion
-    probability; with M independent draws the chance that team t is drawn at
-    least once is 1 - (1 - p_t)^M.
+    [ABS]: a drawn team's terms carry the weight 1/pi; with M independent
+    draws, team t misses every draw with chance (1 - p_t)^M, so it is drawn
+    at least once with chance 1 - (1 - p_t)^M.
     """
     return -math.expm1(M * math.log1p(-p))
 
@@ -525,7 +524,7 @@ def token_scores(q_h, keys):
 
 
 def ht_sums(q_h, team_kv, weights, shift):
-    """Re-weighted sums over the sampled teams ([EXP] steps 4-5; [ABS]; R5).
+    """Weighted sums over the sampled teams ([EXP] steps 4-5; [ABS]; R5).
 
     team_kv: list of (keys [n][d], values [n][d]) for the sampled teams;
     weights: w_t for each (1/pi_t). Returns (numerator [d], denominator):
@@ -560,8 +559,8 @@ def estimate(q_h, team_kv, weights):
 def dense_attention(q_h, keys, vals):
     """Exact softmax attention of one query over all L cached tokens.
 
-    The dense baseline SANTA++ is compared against ([ABS]: the dense-attention
-    baseline). Returns (out [d], lse).
+    The dense baseline SANTA++ is measured against ([ABS] compares with
+    exact attention over every token). Returns (out [d], lse).
     """
     if keys.shape[0] == 0:
         return np.zeros(q_h.shape[0]), -math.inf

@@ -2,13 +2,12 @@
 //
 // Sources:
 //   [ABS] "SANTA++: Sampling Attention through Representative Keys",
-//         arXiv 2609.35629, abstract: exact attention scores inside the
-//         sampled teams; each team's contribution re-weighted by the inverse
-//         of its inclusion probability; the result estimates attention over
-//         the full cache.
+//         arXiv 2609.35629, abstract: only the drawn teams' tokens are
+//         scored, and a drawn team's terms count 1/pi times (pi: its chance
+//         of being drawn), which keeps the sums unbiased.
 //   [EXP] "SANTA++：用代表性 Key 采样把 KV cache 读带宽砍掉 80%" (explainer),
-//         section 三 steps 4-5 (exact scores inside sampled teams, importance
-//         re-weighting).
+//         section 三 steps 4-5 (exact scores inside drawn teams, the 1/pi
+//         weights).
 //
 // Every gather block works for one (sequence b, KV head g) group: it streams
 // the K and V chunks of teams some query head of g drew (dense mode: every

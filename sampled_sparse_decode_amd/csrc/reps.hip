@@ -3,8 +3,8 @@
 // [EXP] "SANTA++：用代表性 Key 采样把 KV cache 读带宽砍掉 80%" (explainer),
 // section 三 step 2: one representative key per team (mean, medoid or random
 // are listed; this library uses the mean). [ABS] "SANTA++: Sampling Attention
-// through Representative Keys", arXiv 2609.35629, abstract: the query scores
-// one representative from each team.
+// through Representative Keys", arXiv 2609.35629, abstract: selection reads
+// these summary keys instead of the whole cache.
 //
 // Mean: rep = round_to_cache_type(sum of the team's n valid keys / n):
 // float64 sums (exact for bfloat16 keys), one correctly rounded float64

@@ -3,9 +3,9 @@
 //
 // Sources:
 //   [ABS] "SANTA++: Sampling Attention through Representative Keys",
-//         arXiv 2609.35629, abstract: the query's score against each team's
-//         representative decides which teams are drawn; a drawn team's terms
-//         carry the weight 1/pi, pi its inclusion probability.
+//         arXiv 2609.35629, abstract: the draws depend only on the query's
+//         dot products with the teams' summary keys; a drawn team's terms
+//         count 1/pi times, pi its chance of being drawn.
 //   [EXP] "SANTA++：用代表性 Key 采样把 KV cache 读带宽砍掉 80%" (explainer),
 //         section 三 steps 2-3: team scores, a softmax over teams, M draws.
 //   [PHX] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
@@ -233,7 +233,7 @@ __device__ __forceinline__ void draw_points(const TailArgs &a, double *pts, int 
 
 // Inclusion probability of drawn team t, from e_t, the cumulative sums C and
 // Z = C_(K-1): independent draws 1 - (1 - p)^M = -expm1(M log1p(-p)) ([ABS]:
-// weights are inverse inclusion probabilities); systematic min(1, M p);
+// the weight of a drawn team is 1/pi); systematic min(1, M p);
 // stratified ([SAN]): in units of 1/M the team covers [a, a + w),
 // a = M C_(t-1) / Z, w = M p, meeting unit floor(a) over
 // q1 = min(w, floor(a) + 1 - a) and the next units over r = w - q1, so

@@ -9,8 +9,8 @@ afresh, as at every decode step):
   - the Horvitz-Thompson denominator and numerator are unbiased: the mean of
     D_hat / D = exp(lse - lse_dense) is 1 and the mean of
     N_hat / D = out * exp(lse - lse_dense) is the dense output, each within
-    five standard errors ("SANTA++", abstract: the re-weighted sampled teams
-    estimate attention over the full cache);
+    five standard errors ("SANTA++", abstract: with the 1/pi weights the
+    drawn teams give an unbiased stand-in for the whole cache's sums);
   - the mean size of a head's drawn set is sum_t pi_t and the mean union of a
     KV head's sets is sum_t (1 - prod_h (1 - p_ht)^M), the closed forms of
     draws with replacement.
