@@ -69,6 +69,13 @@ SMALL = {
     # a full 16-head group over 300 small teams
     "bf16_g16_p300": lambda: W.qwen_planted(batch=1, seq_len=4800, T=16, M=40, hq=16, hkv=1, d=64,
                                                         plants=3),
+    # the largest call the per-head blocks take: 64 (sequence, query head)
+    # pairs over 512-team page tables (one split per head), ragged lengths
+    "bf16_perhead_64heads_p512": lambda: _with_lens(W.qwen_planted(batch=4, seq_len=8192, T=16, M=40, hq=16,
+                                                                   hkv=2, d=64, plants=2), [8192, 8191, 17, 5000]),
+    # per-head blocks under full coverage (M >= K: every team, pi = 1)
+    "bf16_perhead_full_coverage": lambda: W.qwen_planted(batch=2, seq_len=300, T=64, M=8, hq=8, hkv=2, d=128,
+                                                         plants=1),
 }
 
 
@@ -155,7 +162,8 @@ def test_santa_parity(name):
 
 
 @pytest.mark.parametrize("name", ["qwen_bf16_ragged", "mixture_t256", "bf16_g16_p300",
-                                  "f32_d128_t64_g2"])
+                                  "f32_d128_t64_g2", "bf16_perhead_64heads_p512", "bf16_perhead_full_coverage",
+                                  "qwen_mixq_b2", "bf16_b16_t16_union_rank"])
 def test_decode_equals_select_then_attend(name):
     """santa_decode_attention and santa_select_teams + santa_attend_selected on
     one workspace give bit-identical results (sets, weights, outputs)."""
