@@ -24,9 +24,10 @@ constexpr int kUpfrontPasses = 4;                   // page tables up to 512 row
 
 // One block per (sequence b, query head h). Writes the head's team bitmap,
 // log w_t of every drawn team, and the optional sorted list with 1/pi.
-// Blocks are placed by XCD (block i runs on XCD i mod 8; the grid is a
-// multiple of 8 and XCD x takes heads [x n8, (x + 1) n8)), so the G heads
-// of a group, which read the same representative rows, share one L2.
+// Blocks are placed by XCD (block i runs on XCD i mod 8; the grid is 8 n8
+// with n8 a whole number of groups' heads, and XCD x takes heads
+// [x n8, (x + 1) n8)), so the G heads of a group, which read the same
+// representative rows, share one L2.
 template <typename KV, int D, bool UPFRONT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     using Pt = sel::Part<KV, D>;
@@ -148,7 +149,8 @@ __global__ __launch_bounds__(kBlock) void given_kernel(Params p) {
 
 santa_status launch_select(const Params &p, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(unsigned((int64_t(p.B) * p.Hq + 7) / 8 * 8)), block(kSelThreads);
+    const int64_t groups = int64_t(p.B) * p.Hkv;
+    const dim3 grid(unsigned(8 * ((groups + 7) / 8) * p.G)), block(kSelThreads);
     const bool up = p.dtype == SANTA_BF16 && p.P <= kUpfrontPasses * kRowsPerPass;   // float32 rows would spill
 #define SANTA_SELECT_LAUNCH(KV, DD)                                                                            \
     if (up) hipLaunchKernelGGL((select_kernel<KV, DD, true>), grid, block, 0, st, p);                          \
