@@ -61,17 +61,42 @@ def test_graph_replays_match_eager():
 
 @pytest.mark.parametrize("scheme", ["iid", "stratified"])
 def test_graph_captured_decode_loop(scheme):
-    # One serving step captured once and replayed: advance every sequence by
-    # one token (its key and value already in the pages), refresh the
-    # representatives of the touched teams, decode. After each replay the
-    # representatives equal a fresh full build and the outputs equal an
-    # eager decode at the new lengths, bit for bit.
+    # One serving step captured once and replayed: every sequence gets its
+    # next token's key and value (gathered on the device from the plain
+    # pages at the current length) written by santa_append_kv, the lengths
+    # advance, the touched teams' representatives are refreshed, and the
+    # layer is decoded. The cache starts with every position past the start
+    # lengths zeroed. After each replay the representatives equal a fresh
+    # full build and the outputs an eager decode at the new lengths, bit for
+    # bit; at the end the grown tiles equal a fresh pack of the sequences.
     w = W.paged_ragged(num_seqs=3, len_min=500, len_max=1500, T=32, M=16, hq=8, hkv=2, d=128)
     print(f"[graph loop] {scheme}", flush=True)
-    kv, q = S.kv_from_workload(w)
-    final = kv.seq_lens.clone()
     steps = 6
-    kv.seq_lens.sub_(steps + 2)                      # start a few tokens back
+    final = w.seq_lens.astype(np.int64)
+    start = final - (steps + 2)                      # start a few tokens back
+    T = w.page_size
+
+    def truncated(lens):
+        k, v = w.k_pages.copy(), w.v_pages.copy()
+        for b in range(w.batch):
+            for t in range(w.max_pages_per_seq):
+                lo = int(lens[b]) - t * T
+                if lo < T:
+                    k[w.page_table[b, t], :, max(lo, 0):] = 0
+                    v[w.page_table[b, t], :, max(lo, 0):] = 0
+        return k, v
+
+    def cache(k_plain, v_plain, lens):
+        kp, vp = S.pack_pages(S.storage_tensor(k_plain, w.dtype, "cuda"), S.storage_tensor(v_plain, w.dtype, "cuda"))
+        return S.KVCache(kp, vp, torch.from_numpy(w.page_table.astype(np.int32)).cuda(),
+                         torch.from_numpy(lens.astype(np.int32)).cuda(), w.num_q_heads, T)
+
+    kv = cache(*truncated(start), start)
+    q = S.storage_tensor(w.q, w.dtype, "cuda")
+    k_src = S.storage_tensor(w.k_pages, w.dtype, "cuda")         # [pages][Hkv][T][d], every token
+    v_src = S.storage_tensor(w.v_pages, w.dtype, "cuda")
+    table = kv.page_table.long()
+    rows = torch.arange(w.batch, device="cuda")
     reps = S.santa_build_reps(kv)
     prev = kv.seq_lens.clone()
     ws = S.make_workspace(kv, w.M)
@@ -80,7 +105,12 @@ def test_graph_captured_decode_loop(scheme):
 
     def step():
         prev.copy_(kv.seq_lens)
+        pos = prev.long()
+        page = table[rows, pos // T]
+        k_new = k_src[page, :, pos % T, :].unsqueeze(1).contiguous()   # [B][1][Hkv][d]
+        v_new = v_src[page, :, pos % T, :].unsqueeze(1).contiguous()
         kv.seq_lens.add_(1)
+        S.santa_append_kv(kv, prev, k_new, v_new)
         S.santa_update_reps(kv, reps, prev, 1)
         S.santa_decode_attention_ex(kv, q, reps, w.M, scheme, 3, 11, ws, out, lse)
 
@@ -102,4 +132,9 @@ def test_graph_captured_decode_loop(scheme):
         torch.cuda.synchronize()
         assert torch.equal(reps, fresh), f"replay {r}: representatives differ from a full build"
         assert torch.equal(out, o2) and torch.equal(lse, l2), f"replay {r}: outputs differ from eager"
-    assert torch.equal(kv.seq_lens, final - 1)
+    lens = kv.seq_lens.cpu().numpy().astype(np.int64)
+    assert np.array_equal(lens, final - 1)
+    ref = cache(*truncated(lens), lens)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.k_pages.view(torch.int16), ref.k_pages.view(torch.int16)), "grown keys differ from a fresh pack"
+    assert torch.equal(kv.v_pages.view(torch.int16), ref.v_pages.view(torch.int16)), "grown values differ from a fresh pack"
