@@ -70,6 +70,13 @@ Readings taken where the pages leave a step open (each repeated where used):
       divide); after `iters` assignments (no move after the last) the
       assignment is the code, and the tokens are stably sorted by code and
       cut into runs of T as in R11.
+  R13 value samples (optional, [SANTA] abstract): S points per head from
+      their own Philox stream (key word 0 xored with VALUE_KEY_XOR), pushed
+      through the inverse CDF of the drawn tokens' weighted logits in team
+      order, then token order; independent, systematic or stratified points
+      as for the team draws.
+  R14 the value-sampled output is the plain mean of the sampled values; the
+      log-sum-exp stays that of the drawn tokens (the denominator is exact).
 
 Parity pins (tests/test_oracle_pins.py): dense attention against torch's
 scaled_dot_product_attention; full coverage against dense; brute-force
@@ -94,6 +101,11 @@ team-coherent keys both schemes lower the error. R11: code bits against
 basis directions, signs against exact rational dot products, a stable
 order that keeps separated clusters in one run, a per-head permutation
 that leaves dense attention unchanged, lower error on planted keys.
+R13-R14: the sample frequencies over an even grid of points equal the
+token probabilities, the mean over many offsets converges to the SANTA++
+estimate of the same teams, systematic samples give every token of mass
+at least k/S at least k samples, a one-token head returns its value, and
+the value stream differs from the team stream.
 """
 import math
 from fractions import Fraction
@@ -632,6 +644,98 @@ def santa_head(kv, q_h, reps, b, h, num_q_heads, M, seed, offset, scheme=DRAW_II
     sel = select_teams(q_h, rep_rows, M, seed, offset, b, h, scheme)
     out, lse = estimate(q_h, [kv.team(b, g, t) for t in sel.teams], sel.inv_pi)
     return HeadResult(out, lse, sel)
+
+
+# ----------------------------------------------------------------------------
+# Value samples inside the drawn teams (the optional half of the
+# variance-reduced row; [SANTA] abstract; readings R13-R14)
+# ----------------------------------------------------------------------------
+
+VALUE_KEY_XOR = 0x56414C55   # separates the value-sample stream from the team draws (R13)
+
+
+def value_uniforms(scheme, S, seed, offset, b, h):
+    """The S points in (0, 1) that pick one head's value samples (R13).
+
+    Sample k takes word k mod 4 of Philox4x32-10 with counter
+    (k div 4, h, b, offset) and key (seed lo xor VALUE_KEY_XOR, seed hi);
+    u = (x + 1/2) 2^-32. Independent points u_k; systematic (k + u_0) / S;
+    stratified (k + u_k) / S, as for the team draws.
+    """
+    from .philox import philox4x32_10, MASK32, word_to_uniform
+    seed = int(seed)
+    key = ((seed & MASK32) ^ VALUE_KEY_XOR, (seed >> 32) & MASK32)
+    u = [word_to_uniform(philox4x32_10((k // 4, h, b, offset), key)[k % 4]) for k in range(S)]
+    if scheme == DRAW_IID:
+        return u
+    if scheme == DRAW_SYSTEMATIC:
+        return [(k + u[0]) / S for k in range(S)]
+    if scheme == DRAW_STRATIFIED:
+        return [(k + u[k]) / S for k in range(S)]
+    raise ValueError(f"unknown draw scheme {scheme!r}")
+
+
+class ValueSampled:
+    """SANTA++ teams with value samples: the estimate and what decided it."""
+
+    def __init__(self, out, lse, selection, positions, near_tie_positions, logits):
+        self.out, self.lse, self.selection = out, lse, selection
+        self.positions = positions                    # sampled token positions (t * T + j), in sample order
+        self.near_tie_positions = near_tie_positions  # positions a near-tie sample may land on instead
+        self.logits = logits                          # weighted logits of the drawn tokens, team then token order
+
+
+def value_sampled_head(kv, q_h, reps, b, h, num_q_heads, M, S, seed, offset, scheme=DRAW_IID,
+                       value_scheme=DRAW_IID):
+    """SANTA++ team draws, then S value samples inside the drawn teams (R13,
+    R14; [SANTA] abstract: sampling indices from the post-softmax weights and
+    averaging only those value rows estimates the weighted value sum).
+
+    The drawn teams and weights are select_teams'. Over the drawn tokens in
+    team order, then token order, the weighted logits are
+    l_j = s_j + log w_t (s_j = q . k_j / sqrt(d), w_t = 1 / pi_t); with
+    m = max l, e_j = exp(l_j - m) and C the running sums (Z = C_last), sample k
+    takes the first token j with u_k Z < C_j (the team rule, one level down).
+    out = (1/S) sum_k v_(j_k), which given the drawn teams averages to the
+    SANTA++ estimate sum_j (e_j / Z) v_j; lse = m + log Z, the SANTA++ log-sum-exp.
+    Samples within NEAR_TIE of a boundary record the positions they can reach.
+    """
+    g = h // (num_q_heads // kv.hkv)
+    L = int(kv.seq_lens[b])
+    K = num_teams(L, kv.T)
+    if K == 0:
+        return ValueSampled(np.zeros(kv.d), -math.inf, Selection([], [], np.zeros(0), set(), [], True), [], set(),
+                            np.zeros(0))
+    rep_rows = np.stack([reps[b, t, g] for t in range(K)])
+    sel = select_teams(q_h, rep_rows, M, seed, offset, b, h, scheme)
+    logits, vals, pos = [], [], []
+    for t, w in zip(sel.teams, sel.inv_pi):
+        keys, v = kv.team(b, g, t)
+        logits.append(token_scores(q_h, keys) + math.log(w))
+        vals.append(v)
+        pos.extend(t * kv.T + j for j in range(keys.shape[0]))
+    logits = np.concatenate(logits)
+    vals = np.concatenate(vals)
+    e, C, Z, _ = team_softmax(logits)
+    m = float(np.max(logits))
+    picks, near = [], set()
+    for u in value_uniforms(value_scheme, S, seed, offset, b, h):
+        j = inverse_cdf(u, e, C, Z)
+        picks.append(j)
+        near.update(pos[i] for i in near_tie_teams_of_draw(u, e, C, Z))
+    out = np.mean(vals[picks], axis=0)
+    return ValueSampled(out, m + math.log(Z), sel, [pos[j] for j in picks], near, logits)
+
+
+def value_sampled_given(kv, q_h, b, h, num_q_heads, positions):
+    """The value-sampled output for supplied sample positions (a near-tie
+    made the HIP path pick another valid position): their values' mean."""
+    g = h // (num_q_heads // kv.hkv)
+    rows = []
+    for p in positions:
+        _, v = kv.team(b, g, p // kv.T)
+        rows.append(v[p % kv.T])
+    return np.mean(np.stack(rows), axis=0)
 
 
 def evaluate_given_set(kv, q_h, b, h, num_q_heads, teams, inv_pi):

@@ -812,3 +812,121 @@ def test_cluster_pages_kmeans_is_a_permutation_that_keeps_dense_attention():
             o0, l0 = santa.dense_head(kv0, qh, b, h, 4)
             o1, l1 = santa.dense_head(kv1, qh, b, h, 4)
             assert np.max(np.abs(o0 - o1)) < 1e-12 and abs(l0 - l1) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Value samples inside the drawn teams (readings R13-R14)
+# --------------------------------------------------------------------------
+
+def _value_case(M=5, n=700, T=32):
+    w = wl.tiny_planted(n=n, d=32, T=T, M=M)
+    kv = _kv(w)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    return w, kv, reps, numerics.decode(w.q[0, 0], "f32")
+
+
+def _conditional_means(fn, R=3000, S=8):
+    """Mean over R independent value-point sets of fn's output with the team
+    draws held fixed (seed 5, offset 3): the points come from numpy, not
+    Philox, through the oracle's own inverse CDF."""
+    w, kv, reps, qh = _value_case()
+    rng = np.random.default_rng(17)
+    orig = santa.value_uniforms
+    outs = np.empty((R, w.head_dim))
+    try:
+        for r in range(R):
+            pts = list(rng.random(S))
+            santa.value_uniforms = lambda *a, **k: pts
+            outs[r] = fn(kv, qh, reps, 0, 0, 1, w.M, S, 5, 3).out
+    finally:
+        santa.value_uniforms = orig
+    ref = santa.santa_head(kv, qh, reps, 0, 0, 1, w.M, 5, 3)
+    return outs, ref
+
+
+def test_value_samples_average_to_the_santa_estimate_of_the_same_teams():
+    # Given the drawn teams, the mean of the sampled values is unbiased for
+    # the weighted value sum: averaging over many independent point sets
+    # lands on santa_head's estimate (a separate code path: weights multiply
+    # exp(s - shift) there, they shift the logits here).
+    outs, ref = _conditional_means(santa.value_sampled_head)
+    se = outs.std(axis=0) / math.sqrt(len(outs))
+    assert np.all(np.abs(outs.mean(axis=0) - ref.out) < 5 * se + 1e-12)
+    # and the log-sum-exp is that of the drawn tokens
+    w, kv, reps, qh = _value_case()
+    r = santa.value_sampled_head(kv, qh, reps, 0, 0, 1, w.M, 8, 5, 3)
+    assert abs(r.lse - ref.lse) < 1e-12 * max(1.0, abs(ref.lse))
+    assert r.selection.teams == ref.selection.teams
+
+
+def _without_weights(kv, q_h, reps, b, h, Hq, M, S, seed, offset):
+    # planted mistake: the logits without log w
+    r = santa.value_sampled_head(kv, q_h, reps, b, h, Hq, M, S, seed, offset)
+    g = 0
+    logits, vals = [], []
+    for t in r.selection.teams:
+        keys, v = kv.team(b, g, t)
+        logits.append(santa.token_scores(q_h, keys))
+        vals.append(v)
+    logits, vals = np.concatenate(logits), np.concatenate(vals)
+    e, C, Z, _ = santa.team_softmax(logits)
+    picks = [santa.inverse_cdf(u, e, C, Z) for u in santa.value_uniforms(0, S, seed, offset, b, h)]
+    r.out = np.mean(vals[picks], axis=0)
+    return r
+
+
+def test_value_sample_pin_catches_dropped_weights():
+    outs, ref = _conditional_means(_without_weights)
+    se = outs.std(axis=0) / math.sqrt(len(outs))
+    assert np.any(np.abs(outs.mean(axis=0) - ref.out) >= 5 * se + 1e-12)
+
+
+def test_value_samples_under_full_coverage_average_to_dense_attention():
+    # Every team read (M >= K, w = 1): the samples come from the exact
+    # attention weights, so their mean over many offsets is dense attention.
+    w, kv, reps, qh = _value_case(M=64, n=300, T=32)
+    keys, vals = kv.all_tokens(0, 0)
+    out_d, lse_d = santa.dense_attention(qh, keys, vals)
+    R, S = 3000, 4
+    outs = np.stack([santa.value_sampled_head(kv, qh, reps, 0, 0, 1, w.M, S, 9, off).out for off in range(R)])
+    se = outs.std(axis=0) / math.sqrt(R)
+    assert np.all(np.abs(outs.mean(axis=0) - out_d) < 5 * se + 1e-12)
+    r = santa.value_sampled_head(kv, qh, reps, 0, 0, 1, w.M, S, 9, 0)
+    assert abs(r.lse - lse_d) < 1e-12 * max(1.0, abs(lse_d))
+
+
+def test_systematic_value_samples_follow_the_token_probabilities():
+    # One point per unit of width 1/S: token j is sampled floor(S p_j) or
+    # ceil(S p_j) times.
+    w, kv, reps, qh = _value_case()
+    S = 64
+    r = santa.value_sampled_head(kv, qh, reps, 0, 0, 1, w.M, S, 5, 3, value_scheme=santa.DRAW_SYSTEMATIC)
+    p = np.exp(r.logits - r.logits.max())
+    p /= p.sum()
+    pos = []
+    for t in r.selection.teams:
+        n = santa.team_size(int(w.seq_lens[0]), w.page_size, t)
+        pos.extend(t * w.page_size + j for j in range(n))
+    counts = np.array([r.positions.count(x) for x in pos])
+    assert counts.sum() == S
+    assert np.all(counts >= np.floor(S * p - 1e-9)) and np.all(counts <= np.ceil(S * p + 1e-9))
+
+
+def test_value_samples_of_a_one_token_sequence():
+    import dataclasses
+    w = dataclasses.replace(wl.tiny_planted(n=64, d=32, T=32, M=4), seq_lens=np.array([1], dtype=np.int32))
+    kv = _kv(w)
+    reps = santa.build_reps(w.k_pages, w.page_table, w.seq_lens, w.page_size, w.dtype)
+    qh = numerics.decode(w.q[0, 0], "f32")
+    r = santa.value_sampled_head(kv, qh, reps, 0, 0, 1, w.M, 5, 1, 0)
+    keys, vals = kv.all_tokens(0, 0)
+    assert r.positions == [0] * 5
+    assert np.array_equal(r.out, vals[0])
+    assert r.lse == pytest.approx(float(santa.token_scores(qh, keys)[0]), abs=1e-12)
+
+
+def test_value_stream_differs_from_the_team_stream():
+    for scheme in (santa.DRAW_IID, santa.DRAW_SYSTEMATIC, santa.DRAW_STRATIFIED):
+        a = santa.value_uniforms(scheme, 16, 7, 2, 1, 3)
+        b = santa.draw_uniforms(scheme, 16, 7, 2, 1, 3)
+        assert all(0.0 < x < 1.0 for x in a) and len(set(a) & set(b)) == 0
