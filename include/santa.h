@@ -314,6 +314,38 @@ santa_status santa_attend_selected(const santa_kv *kv, const void *q, int32_t M,
                                    float *out, float *lse,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* SANTA++ team draws, then value samples inside the drawn teams ([ABS] for
+ * the teams and their 1/pi weights; "Stochastic Sparse Attention for
+ * Memory-Bound Inference" (the SANTA page), abstract: drawing token indices
+ * from the post-softmax weights and averaging only their value rows
+ * estimates the weighted value sum without bias, with stratified and
+ * systematic points as lower-variance choices). The teams, their weights
+ * and the optional sorted set are those of santa_select_teams_ex with
+ * `scheme`. Over the drawn tokens, in team order then token order, the
+ * weighted logits are l_g = q . k_g / sqrt(d) + log w_t (float64 scores,
+ * w_t as stored by the selection: the float32 -log(pi_t)); with
+ * e_g = exp(l_g - max l) and C their running sums, value sample k takes the
+ * first token g with point_k * C_last < C_g, point_k from Philox4x32-10 word
+ * k mod 4 of counter (k / 4, h, b, offset) and key (seed lo ^ 0x56414C55,
+ * seed hi), u = (x + 1/2) 2^-32, and (k + u_0) / S or (k + u_k) / S for the
+ * systematic and stratified `value_scheme`. Then
+ *   out[b][h] = (1 / S) sum_k v(g_k)       float32
+ *   lse[b][h] = max l + log C_last          float32 (the drawn tokens' exact
+ *                                           log-sum-exp, as santa_decode_attention)
+ *   positions [B][Hq][S] int32 or NULL: sampled token positions t * T + j,
+ *             in sample order (-1 for an empty sequence)
+ * Given the drawn teams, out averages to santa_decode_attention's output
+ * (the value samples add their own variance). Reads the drawn teams' keys
+ * and only the value lines the samples touch. Needs
+ * min(M, max_pages_per_seq) * page_size <= 16384 (SANTA_ERR_UNSUPPORTED
+ * otherwise) and 1 <= S <= 256 (SANTA_ERR_SHAPE); other arguments as for
+ * santa_decode_attention_ex. Two launches. */
+santa_status santa_decode_attention_value_sampled(const santa_kv *kv, const void *q, const void *reps,
+                                                 int32_t M, int32_t scheme, int32_t S, int32_t value_scheme,
+                                                 uint64_t seed, uint32_t offset, float *out, float *lse,
+                                                 int32_t *sampled, float *inv_pi, int32_t *positions,
+                                                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* Dense decode attention over every cached token: the baseline SANTA++ is
  * compared with ([ABS]: the dense attention baseline). Same kernels as step 5
  * above with every team taken and w = 1.

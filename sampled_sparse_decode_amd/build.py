@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsanta.so")
 ARCH = "gfx950"
 
-SOURCES = ["santa_api.cpp", "reps.hip", "select.hip", "gather.hip", "pack.hip", "cluster.hip", "noalloc.hip"]
+SOURCES = ["santa_api.cpp", "reps.hip", "select.hip", "gather.hip", "pack.hip", "cluster.hip", "noalloc.hip",
+           "value.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

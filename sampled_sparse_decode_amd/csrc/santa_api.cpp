@@ -300,6 +300,35 @@ santa_status santa_select_teams_ex(const santa_kv *kv, const void *q, const void
     return launch_select(p, stream);
 }
 
+santa_status santa_decode_attention_value_sampled(const santa_kv *kv, const void *q, const void *reps,
+                                                 int32_t M, int32_t scheme, int32_t S, int32_t value_scheme,
+                                                 uint64_t seed, uint32_t offset, float *out, float *lse,
+                                                 int32_t *sampled, float *inv_pi, int32_t *positions,
+                                                 void *workspace, size_t workspace_bytes, void *stream) {
+    Params p;
+    santa_status st = santa_params(kv, q, M, out, lse, workspace, workspace_bytes, &p);
+    if (st != SANTA_OK) return st;
+    if (!reps || !out) return SANTA_ERR_NULL;
+    if ((sampled == nullptr) != (inv_pi == nullptr)) return SANTA_ERR_NULL;
+    for (int32_t sc : {scheme, value_scheme})
+        if (sc != SANTA_DRAW_IID && sc != SANTA_DRAW_SYSTEMATIC && sc != SANTA_DRAW_STRATIFIED) return SANTA_ERR_SHAPE;
+    if (S < 1 || S > kVsMaxSamples) return SANTA_ERR_SHAPE;
+    if (int64_t(std::min(M, kv->max_pages_per_seq)) * kv->page_size > kVsMaxTokens) return SANTA_ERR_UNSUPPORTED;
+    p.scheme = scheme;
+    p.reps = reps;
+    p.seed_lo = uint32_t(seed & 0xffffffffu);
+    p.seed_hi = uint32_t(seed >> 32);
+    p.offset = offset;
+    p.sampled = sampled;
+    p.inv_pi = inv_pi;
+    p.vs_samples = S;
+    p.vs_scheme = value_scheme;
+    p.vs_positions = positions;
+    st = launch_select(p, stream);
+    if (st != SANTA_OK) return st;
+    return launch_value_sample(p, stream);
+}
+
 santa_status santa_select_teams(const santa_kv *kv, const void *q, const void *reps,
                                 int32_t M, uint64_t seed, uint32_t offset,
                                 int32_t *sampled, float *inv_pi,
@@ -574,6 +603,6 @@ const char *santa_status_string(int32_t status) {
     }
 }
 
-int32_t santa_version(void) { return 250; }
+int32_t santa_version(void) { return 260; }
 
 }  // extern "C"

@@ -17,6 +17,8 @@ constexpr int kMaxTeamsPerSplit = 16;
 constexpr int kSantaWaves = 8;         // wavefronts per SANTA++ union-gather block (bfloat16)
 constexpr int kPerHeadMaxTeams = 512;  // per-head gather: page-table rows at most
 constexpr int kPerHeadMaxHeads = 64;   // per-head gather: (sequence, query head) pairs per call at most
+constexpr int kVsMaxTokens = 16384;    // value samples: drawn tokens per head at most (min(M, P) * T)
+constexpr int kVsMaxSamples = 256;     // value samples per head at most
 
 enum Mode : int32_t { kModeSanta = 0, kModeDense = 1 };
 
@@ -89,6 +91,9 @@ struct Params {
     int32_t scheme;             // santa_draw_scheme of select launches
     int32_t per_head;           // 1 (bf16): blocks per (head, range), each head streaming its own teams
     int32_t fused;              // per-head blocks select their head's teams themselves (one-launch decode)
+    int32_t vs_samples;         // value samples per head (santa_decode_attention_value_sampled)
+    int32_t vs_scheme;          // santa_draw_scheme of the value samples
+    int32_t *vs_positions;      // [B][Hq][vs_samples] sampled token positions, or NULL
 };
 
 constexpr uint32_t kRepKeyXor = 0x52455053u;   // random representatives: key word 0 = seed lo ^ this
@@ -150,6 +155,7 @@ santa_status launch_select(const Params &p, void *stream);
 santa_status launch_given(const Params &p, void *stream);
 santa_status launch_gather(const Params &p, void *stream);
 santa_status launch_combine(const Params &p, void *stream);
+santa_status launch_value_sample(const Params &p, void *stream);
 santa_status launch_pack_pages(const PackParams &pp, void *stream);
 santa_status launch_append_kv(const AppendParams &ap, void *stream);
 santa_status launch_pack_hashed(const ClusterParams &c, void *stream);

@@ -27,6 +27,7 @@ EXPORTED = (
     "santa_decode_attention",
     "santa_decode_attention_ex",
     "santa_decode_attention_noalloc",
+    "santa_decode_attention_value_sampled",
     "santa_select_teams",
     "santa_select_teams_ex",
     "santa_attend_selected",
@@ -96,6 +97,8 @@ def declare_signatures(lib):
         "santa_decode_attention": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P, sz, P]),
         "santa_decode_attention_ex": (i32, [kvp, P, P, i32, u64, u32, i32, P, P, P, P, P, sz, P]),
         "santa_decode_attention_noalloc": (i32, [kvp, P, P, i32, u64, u32, P, P, P, P, P]),
+        "santa_decode_attention_value_sampled": (i32, [kvp, P, P, i32, i32, i32, i32, u64, u32, P, P, P, P, P,
+                                                       P, sz, P]),
         "santa_select_teams": (i32, [kvp, P, P, i32, u64, u32, P, P, P, sz, P]),
         "santa_select_teams_ex": (i32, [kvp, P, P, i32, u64, u32, i32, P, P, P, sz, P]),
         "santa_attend_selected": (i32, [kvp, P, i32, P, P, P, sz, P]),
@@ -482,6 +485,45 @@ def _decode(kv, q, reps, M, seed, offset, scheme, workspace, out, lse, return_se
     if return_sets:
         return out, lse, sampled, inv_pi
     return out, lse
+
+
+def santa_decode_attention_value_sampled(kv, q, reps, M, S, scheme="iid", value_scheme="iid", seed=0, offset=0,
+                                         workspace=None, out=None, lse=None, return_sets=False,
+                                         return_positions=False):
+    """SANTA++ team draws, then S value samples inside the drawn teams (the
+    mean of the sampled tokens' values). Returns (out, lse), followed by
+    (sampled, inv_pi) when return_sets and by positions [B][Hq][S] when
+    return_positions."""
+    _check_q(kv, q)
+    _check_reps(kv, reps)
+    _check_outputs(kv, out, lse)
+    _check_workspace(workspace, kv)
+    B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
+    dev = kv.device
+    if workspace is None:
+        workspace = make_workspace(kv, M)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    sampled = inv_pi = positions = None
+    if return_sets:
+        sampled = torch.empty((B, Hq, M), dtype=torch.int32, device=dev)
+        inv_pi = torch.empty((B, Hq, M), dtype=torch.float32, device=dev)
+    if return_positions:
+        positions = torch.empty((B, Hq, max(int(S), 1)), dtype=torch.int32, device=dev)
+    desc = kv.desc()
+    st = load().santa_decode_attention_value_sampled(
+        ctypes.byref(desc), _ptr(q), _ptr(reps), int(M), _scheme_code(scheme), int(S), _scheme_code(value_scheme),
+        int(seed), int(offset), _ptr(out), _ptr(lse), _ptr(sampled), _ptr(inv_pi), _ptr(positions),
+        _ptr(workspace), workspace.numel(), _stream())
+    _check("santa_decode_attention_value_sampled", st)
+    res = (out, lse)
+    if return_sets:
+        res += (sampled, inv_pi)
+    if return_positions:
+        res += (positions,)
+    return res
 
 
 def santa_decode_attention_noalloc(kv, q, reps, M, seed=0, offset=0, out=None, lse=None, sampled=None,

@@ -30,6 +30,7 @@ santa_status launch_select(const Params &p, void *) { return touch(p); }
 santa_status launch_given(const Params &p, void *) { return touch(p); }
 santa_status launch_gather(const Params &p, void *) { return touch(p); }
 santa_status launch_combine(const Params &p, void *) { return touch(p); }
+santa_status launch_value_sample(const Params &p, void *) { return touch(p); }
 santa_status launch_pack_pages(const PackParams &pp, void *) { return touch(pp); }
 santa_status launch_append_kv(const AppendParams &ap, void *) { return touch(ap); }
 santa_status launch_pack_hashed(const ClusterParams &c, void *) { return touch(c); }

@@ -81,7 +81,21 @@ def check_santa_head(w, kv, reps, b, h, out, lse, teams, inv_pi, M=None, seed=No
     offset = w.offset if offset is None else offset
     qh = numerics.decode(w.q[b, h], w.dtype)
     res = santa.santa_head(kv, qh, reps, b, h, w.num_q_heads, M, seed, offset, scheme)
-    sel = res.selection
+    got_teams, ref_w, flip = _check_sets(res.selection, b, h, teams, inv_pi, M, scheme)
+    if flip:
+        ref_out, ref_lse = santa.evaluate_given_set(kv, qh, b, h, w.num_q_heads, got_teams, ref_w)
+    else:
+        ref_out, ref_lse = res.out, res.lse
+    err = float(np.max(np.abs(out - ref_out))) if len(ref_out) else 0.0
+    assert err <= OUT_TOL[w.dtype], f"santa (b={b}, h={h}) max-abs {err}"
+    _check_lse(w, lse, ref_lse, b, h)
+    return err, flip
+
+
+def _check_sets(sel, b, h, teams, inv_pi, M, scheme):
+    """The HIP team list (ascending, -1 padded) against the oracle's selection:
+    equal, or different only in near-tie teams; the weights 1/pi of the HIP
+    teams within INV_PI_RTOL. Returns (HIP teams, their exact weights, flip)."""
     got_teams = [int(t) for t in teams if t >= 0]
     assert all(t < 0 for t in teams[len(got_teams):]), "sampled list not -1 padded"
     assert got_teams == sorted(set(got_teams)), "sampled list not ascending and unique"
@@ -98,11 +112,45 @@ def check_santa_head(w, kv, reps, b, h, out, lse, teams, inv_pi, M=None, seed=No
     w_got = np.asarray(inv_pi[:len(got_teams)], dtype=np.float64)
     assert np.all(np.abs(w_got - ref_w) <= INV_PI_RTOL * np.abs(ref_w) + 1e-30), f"(b={b}, h={h}) 1/pi differs"
     assert np.all(np.asarray(inv_pi[len(got_teams):]) == 0.0)
+    return got_teams, ref_w, flip
+
+
+def check_value_sampled_head(w, kv, reps, b, h, S, out, lse, teams, inv_pi, positions, M=None, seed=None,
+                             offset=None, scheme=santa.DRAW_IID, value_scheme=santa.DRAW_IID):
+    """One head of santa_decode_attention_value_sampled against the oracle.
+
+    Teams and weights as for SANTA++; the S sample positions must equal the
+    oracle's, except that a sample within NEAR_TIE of a token boundary may
+    take another token it can reach (both listed as near-tie positions). On a
+    near-tie team flip the logits differ, so each position is only checked to
+    lie in a HIP team. The output is compared with the mean of the values at
+    the HIP positions (the oracle's own when they agree); the log-sum-exp
+    with the oracle's on the HIP team set. Returns (max-abs error, flips).
+    """
+    M = w.M if M is None else M
+    seed = w.seed if seed is None else seed
+    offset = w.offset if offset is None else offset
+    qh = numerics.decode(w.q[b, h], w.dtype)
+    res = santa.value_sampled_head(kv, qh, reps, b, h, w.num_q_heads, M, S, seed, offset, scheme, value_scheme)
+    L = int(w.seq_lens[b])
+    got = [int(x) for x in positions[:S]]
+    if L == 0:
+        assert got == [-1] * S, f"(b={b}, h={h}) positions of an empty sequence {got}"
+        assert np.all(out == 0.0) and lse == -math.inf
+        return 0.0, 0
+    got_teams, ref_w, flip = _check_sets(res.selection, b, h, teams, inv_pi, M, scheme)
+    assert all(0 <= x < L and x // w.page_size in got_teams for x in got), f"(b={b}, h={h}) positions {got}"
+    flips = int(flip)
     if flip:
-        ref_out, ref_lse = santa.evaluate_given_set(kv, qh, b, h, w.num_q_heads, got_teams, ref_w)
+        ref_lse = santa.evaluate_given_set(kv, qh, b, h, w.num_q_heads, got_teams, ref_w)[1]
     else:
-        ref_out, ref_lse = res.out, res.lse
-    err = float(np.max(np.abs(out - ref_out))) if len(ref_out) else 0.0
-    assert err <= OUT_TOL[w.dtype], f"santa (b={b}, h={h}) max-abs {err}"
+        ref_lse = res.lse
+        bad = [(x, y) for x, y in zip(got, res.positions) if x != y]
+        assert all(x in res.near_tie_positions and y in res.near_tie_positions for x, y in bad), (
+            f"(b={b}, h={h}) sample positions differ outside near-ties: {bad[:4]}")
+        flips += len(bad)
+    ref_out = res.out if got == res.positions else santa.value_sampled_given(kv, qh, b, h, w.num_q_heads, got)
+    err = float(np.max(np.abs(out - ref_out)))
+    assert err <= OUT_TOL[w.dtype], f"value-sampled (b={b}, h={h}) max-abs {err}"
     _check_lse(w, lse, ref_lse, b, h)
-    return err, flip
+    return err, flips

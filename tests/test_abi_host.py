@@ -55,7 +55,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.santa_version() == 250
+    assert lib.santa_version() == 260
     for code in range(6):
         assert S.santa_status_string(code)
     assert S.santa_status_string(99) == "unknown status"
@@ -191,6 +191,28 @@ def test_update_reps_validation(lib):
     assert lib.santa_update_reps(ctypes.byref(k), F, F, -1, None) == SHAPE
     assert lib.santa_update_reps(ctypes.byref(k), F, F, 0, None) == OK
     assert lib.santa_update_reps(ctypes.byref(kv(page_size=48)), F, F, 1, None) == UNSUP
+
+
+def test_value_sampled_validation(lib):
+    """santa_decode_attention_value_sampled: sample counts, schemes and the
+    drawn-token bound are checked on the host."""
+    k = kv(batch=1)
+    F = ctypes.c_void_p(FAKE)
+    big = 1 << 40
+    call = lib.santa_decode_attention_value_sampled
+
+    def go(kvx=k, M=31, scheme=0, S=32, vscheme=0, sampled=None, inv_pi=None, reps=F, out=F):
+        return call(ctypes.byref(kvx), F, reps, M, scheme, S, vscheme, 1, 2, out, F, sampled, inv_pi, None, F, big, None)
+    assert go(reps=None) == NULL
+    assert go(out=None) == NULL
+    assert go(sampled=F) == NULL                         # sets come in pairs
+    assert go(S=0) == SHAPE
+    assert go(S=257) == SHAPE
+    assert go(scheme=3) == SHAPE
+    assert go(vscheme=-1) == SHAPE
+    assert go(M=0) == SHAPE
+    assert go(M=129) == UNSUP                            # 129 teams x 128 tokens > 16384
+    assert go(kvx=kv(batch=1, page_size=256, max_pages_per_seq=65), M=500) == UNSUP   # 65 x 256 > 16384
 
 
 def test_append_kv_validation(lib):
