@@ -314,6 +314,15 @@ santa_status santa_attend_selected(const santa_kv *kv, const void *q, int32_t M,
                                    float *out, float *lse,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes of santa_decode_attention_value_sampled for this kv and
+ * M: the selection's sections followed by the per-chunk running sums
+ * (8 bytes per drawn-token slot, ceil(min(M, max_pages_per_seq) * page_size
+ * / 512) * 512 slots per (sequence, query head)), the chunks' (max, total)
+ * pairs and the running sum at every 16-token piece's end (at least
+ * santa_workspace_size's bytes). SANTA_ERR_UNSUPPORTED when
+ * min(M, max_pages_per_seq) * page_size > 16384. */
+santa_status santa_value_sampled_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes);
+
 /* SANTA++ team draws, then value samples inside the drawn teams ([ABS] for
  * the teams and their 1/pi weights; "Stochastic Sparse Attention for
  * Memory-Bound Inference" (the SANTA page), abstract: drawing token indices
@@ -336,10 +345,14 @@ santa_status santa_attend_selected(const santa_kv *kv, const void *q, int32_t M,
  *             in sample order (-1 for an empty sequence)
  * Given the drawn teams, out averages to santa_decode_attention's output
  * (the value samples add their own variance). Reads the drawn teams' keys
- * and only the value lines the samples touch. Needs
+ * and only the value lines the samples touch. The running sums C are formed
+ * per 512-token chunk of the drawn tokens and the chunk totals then added in
+ * chunk order (equal to the flat sums up to rounding). Needs
  * min(M, max_pages_per_seq) * page_size <= 16384 (SANTA_ERR_UNSUPPORTED
- * otherwise) and 1 <= S <= 256 (SANTA_ERR_SHAPE); other arguments as for
- * santa_decode_attention_ex. Two launches. */
+ * otherwise), 1 <= S <= 256 (SANTA_ERR_SHAPE) and a workspace of at least
+ * santa_value_sampled_workspace_size bytes (SANTA_ERR_WORKSPACE); other
+ * arguments as for santa_decode_attention_ex. Three launches (selection,
+ * chunk logits, samples). */
 santa_status santa_decode_attention_value_sampled(const santa_kv *kv, const void *q, const void *reps,
                                                  int32_t M, int32_t scheme, int32_t S, int32_t value_scheme,
                                                  uint64_t seed, uint32_t offset, float *out, float *lse,

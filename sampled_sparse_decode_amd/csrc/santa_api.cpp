@@ -59,6 +59,19 @@ static int32_t teams_per_split(int64_t team_slots, int64_t target) {
     return tps;
 }
 
+size_t value_workspace_layout(const santa_kv &kv, int32_t M, size_t *cs_off, size_t *sum_off, size_t *piece_off,
+                              int32_t *chunks) {
+    const WorkspaceLayout w = workspace_layout(kv);
+    const int64_t tokens = int64_t(std::min(M, kv.max_pages_per_seq)) * kv.page_size;
+    const int64_t nc = (tokens + kVsChunk - 1) / kVsChunk;
+    const size_t heads = size_t(kv.batch) * kv.num_q_heads;
+    *chunks = int32_t(nc);
+    *cs_off = w.part_ml;
+    *sum_off = align256(*cs_off + heads * size_t(nc) * kVsChunk * 8);
+    *piece_off = align256(*sum_off + heads * size_t(nc) * 16);
+    return std::max(w.total, align256(*piece_off + heads * size_t(nc) * (kVsChunk / 16) * 8));
+}
+
 // Split shapes. bfloat16 caches use balanced blocks: each (sequence, KV
 // head) group gets nb blocks that split the group's chunks (32-token pieces
 // of its drawn teams, or of every team for dense) into even contiguous
@@ -300,6 +313,18 @@ santa_status santa_select_teams_ex(const santa_kv *kv, const void *q, const void
     return launch_select(p, stream);
 }
 
+santa_status santa_value_sampled_workspace_size(const santa_kv *kv, int32_t M, size_t *bytes) {
+    santa_status st = validate_kv(kv);
+    if (st != SANTA_OK) return st;
+    if (!bytes) return SANTA_ERR_NULL;
+    if (M < 1) return SANTA_ERR_SHAPE;
+    if (int64_t(std::min(M, kv->max_pages_per_seq)) * kv->page_size > kVsMaxTokens) return SANTA_ERR_UNSUPPORTED;
+    size_t cs_off, sum_off, piece_off;
+    int32_t chunks;
+    *bytes = value_workspace_layout(*kv, M, &cs_off, &sum_off, &piece_off, &chunks);
+    return SANTA_OK;
+}
+
 santa_status santa_decode_attention_value_sampled(const santa_kv *kv, const void *q, const void *reps,
                                                  int32_t M, int32_t scheme, int32_t S, int32_t value_scheme,
                                                  uint64_t seed, uint32_t offset, float *out, float *lse,
@@ -314,6 +339,12 @@ santa_status santa_decode_attention_value_sampled(const santa_kv *kv, const void
         if (sc != SANTA_DRAW_IID && sc != SANTA_DRAW_SYSTEMATIC && sc != SANTA_DRAW_STRATIFIED) return SANTA_ERR_SHAPE;
     if (S < 1 || S > kVsMaxSamples) return SANTA_ERR_SHAPE;
     if (int64_t(std::min(M, kv->max_pages_per_seq)) * kv->page_size > kVsMaxTokens) return SANTA_ERR_UNSUPPORTED;
+    size_t cs_off, sum_off, piece_off;
+    if (workspace_bytes < value_workspace_layout(*kv, M, &cs_off, &sum_off, &piece_off, &p.vs_chunks))
+        return SANTA_ERR_WORKSPACE;
+    p.vs_cs = reinterpret_cast<double *>(static_cast<char *>(workspace) + cs_off);
+    p.vs_sum = reinterpret_cast<double *>(static_cast<char *>(workspace) + sum_off);
+    p.vs_piece = reinterpret_cast<double *>(static_cast<char *>(workspace) + piece_off);
     p.scheme = scheme;
     p.reps = reps;
     p.seed_lo = uint32_t(seed & 0xffffffffu);

@@ -19,6 +19,8 @@ constexpr int kPerHeadMaxTeams = 512;  // per-head gather: page-table rows at mo
 constexpr int kPerHeadMaxHeads = 64;   // per-head gather: (sequence, query head) pairs per call at most
 constexpr int kVsMaxTokens = 16384;    // value samples: drawn tokens per head at most (min(M, P) * T)
 constexpr int kVsMaxSamples = 256;     // value samples per head at most
+constexpr int kVsChunk = 512;          // value samples: drawn tokens per logit block (a multiple of every T)
+constexpr int kVsMaxChunks = kVsMaxTokens / kVsChunk;
 
 enum Mode : int32_t { kModeSanta = 0, kModeDense = 1 };
 
@@ -42,6 +44,11 @@ constexpr int kSpreadBlocks = 256;
 constexpr int kMaxSpreadGroups = 256;
 
 WorkspaceLayout workspace_layout(const santa_kv &kv);
+// Value samples: the selection's sections, then the running sums, chunk
+// pairs and piece ends over the (unused) partial sections; returns the bytes
+// and the three offsets.
+size_t value_workspace_layout(const santa_kv &kv, int32_t M, size_t *cs_off, size_t *sum_off, size_t *piece_off,
+                              int32_t *chunks);
 // The same sections with `slots` partial slots per head (the splits one
 // launch uses), for a workspace sized to a single call.
 WorkspaceLayout workspace_layout(const santa_kv &kv, int32_t slots);
@@ -94,6 +101,10 @@ struct Params {
     int32_t vs_samples;         // value samples per head (santa_decode_attention_value_sampled)
     int32_t vs_scheme;          // santa_draw_scheme of the value samples
     int32_t *vs_positions;      // [B][Hq][vs_samples] sampled token positions, or NULL
+    int32_t vs_chunks;          // logit blocks per head: ceil(min(M, P) T / kVsChunk)
+    double *vs_cs;              // [B][Hq][vs_chunks * kVsChunk] running sums inside each chunk
+    double *vs_sum;             // [B][Hq][vs_chunks] (max, sum) pairs of the chunks
+    double *vs_piece;           // [B][Hq][vs_chunks][kVsChunk / 16] running sum at each 16-token piece's end
 };
 
 constexpr uint32_t kRepKeyXor = 0x52455053u;   // random representatives: key word 0 = seed lo ^ this

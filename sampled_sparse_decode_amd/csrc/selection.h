@@ -121,6 +121,27 @@ __device__ __forceinline__ double part_dot_raw(const uint4 (&raw)[Part<KV, D>::L
     return a0 + a1;
 }
 
+// The same sum with the part's query values held as float32 (the query is a
+// float32 value; each is widened as it is used, so the products are those
+// of the float64 form).
+template <typename KV, int D>
+__device__ __forceinline__ double part_dot_raw(const uint4 (&raw)[Part<KV, D>::LOADS],
+                                               const float (&q)[Part<KV, D>::N]) {
+    constexpr int VPC = Part<KV, D>::VPC;
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+    for (int j = 0; j < Part<KV, D>::LOADS; ++j) {
+        float f[8];
+        unpack(raw[j], f, KV{});
+#pragma unroll
+        for (int e = 0; e < VPC; e += 2) {
+            a0 = fma(double(f[e]), double(q[j * VPC + e]), a0);
+            a1 = fma(double(f[e + 1]), double(q[j * VPC + e + 1]), a1);
+        }
+    }
+    return a0 + a1;
+}
+
 // Score of a row from its four parts' sums (lanes 4i .. 4i + 3); every lane
 // of the quad gets the same value.
 __device__ __forceinline__ double row_score(double pk, double scale) {

@@ -20,6 +20,7 @@ _DTYPES = {torch.float32: SANTA_F32, torch.bfloat16: SANTA_BF16}
 
 EXPORTED = (
     "santa_workspace_size",
+    "santa_value_sampled_workspace_size",
     "santa_build_reps",
     "santa_update_reps",
     "santa_append_kv",
@@ -90,6 +91,7 @@ def declare_signatures(lib):
     i32, u32, u64, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t
     sigs = {
         "santa_workspace_size": (i32, [kvp, i32, ctypes.POINTER(sz)]),
+        "santa_value_sampled_workspace_size": (i32, [kvp, i32, ctypes.POINTER(sz)]),
         "santa_build_reps": (i32, [kvp, P, P]),
         "santa_update_reps": (i32, [kvp, P, P, i32, P]),
         "santa_append_kv": (i32, [kvp, P, P, P, i32, P]),
@@ -324,6 +326,18 @@ def make_workspace(kv, M=1):
     return torch.empty(santa_workspace_size(kv, M), dtype=torch.uint8, device=kv.device)
 
 
+def santa_value_sampled_workspace_size(kv, M):
+    d = kv.desc()
+    n = ctypes.c_size_t(0)
+    _check("santa_value_sampled_workspace_size",
+           load().santa_value_sampled_workspace_size(ctypes.byref(d), int(M), ctypes.byref(n)))
+    return n.value
+
+
+def make_value_sampled_workspace(kv, M):
+    return torch.empty(santa_value_sampled_workspace_size(kv, M), dtype=torch.uint8, device=kv.device)
+
+
 def santa_build_reps(kv, reps=None):
     """Mean key per (sequence, team, KV head), rounded to the cache dtype: [B][P][Hkv][d]."""
     if reps is None:
@@ -501,7 +515,7 @@ def santa_decode_attention_value_sampled(kv, q, reps, M, S, scheme="iid", value_
     B, Hq, d = kv.batch, kv.num_q_heads, kv.head_dim
     dev = kv.device
     if workspace is None:
-        workspace = make_workspace(kv, M)
+        workspace = make_value_sampled_workspace(kv, M)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     if lse is None:

@@ -61,11 +61,15 @@ static void run_shape(int32_t dtype, int32_t batch, int32_t hq, int32_t hkv, int
         /* value samples need every drawn token's logit on chip: at most 16384 tokens per head */
         const int64_t drawn = (int64_t)(M < P ? M : P) * T;
         const santa_status want = drawn <= 16384 ? SANTA_OK : SANTA_ERR_UNSUPPORTED;
+        size_t vws = 0;
+        EXPECT(santa_value_sampled_workspace_size(&kv, M, &vws) == want);
+        if (want == SANTA_OK) EXPECT(vws >= ws);
+        else vws = ws;
         EXPECT(santa_decode_attention_value_sampled(&kv, fp(9), fp(5), M, SANTA_DRAW_IID, 32, SANTA_DRAW_SYSTEMATIC,
                                                     1, 2, (float *)fp(10), (float *)fp(11), (int32_t *)fp(12),
-                                                    (float *)fp(13), (int32_t *)fp(23), fp(14), ws, NULL) == want);
+                                                    (float *)fp(13), (int32_t *)fp(23), fp(14), vws, NULL) == want);
         EXPECT(santa_decode_attention_value_sampled(&kv, fp(9), fp(5), M, SANTA_DRAW_STRATIFIED, 1, SANTA_DRAW_IID,
-                                                    1, 2, (float *)fp(10), NULL, NULL, NULL, NULL, fp(14), ws,
+                                                    1, 2, (float *)fp(10), NULL, NULL, NULL, NULL, fp(14), vws,
                                                     NULL) == want);
     }
     EXPECT(santa_select_teams(&kv, fp(9), fp(5), M, 1, 2, (int32_t *)fp(12), (float *)fp(13), fp(14), ws,

@@ -213,6 +213,27 @@ def test_value_sampled_validation(lib):
     assert go(M=0) == SHAPE
     assert go(M=129) == UNSUP                            # 129 teams x 128 tokens > 16384
     assert go(kvx=kv(batch=1, page_size=256, max_pages_per_seq=65), M=500) == UNSUP   # 65 x 256 > 16384
+    n = ctypes.c_size_t(0)
+    assert lib.santa_value_sampled_workspace_size(ctypes.byref(k), 31, ctypes.byref(n)) == OK
+    small = n.value
+    assert small >= lib_workspace(lib, k, 31)
+    # selection sections, then 31 x 128 tokens -> 8 chunks of 512 running sums per head, and 8 (max, sum) pairs
+    assert lib.santa_value_sampled_workspace_size(ctypes.byref(k), 128, ctypes.byref(n)) == OK
+    assert n.value >= small
+    assert lib.santa_value_sampled_workspace_size(ctypes.byref(k), 129, ctypes.byref(n)) == UNSUP
+    assert lib.santa_value_sampled_workspace_size(ctypes.byref(k), 0, ctypes.byref(n)) == SHAPE
+    # a workspace big enough for the decode but not for the running sums
+    # (64 teams x 256 tokens x 8 bytes per head exceed the d = 64 partials)
+    k2 = kv(batch=1, head_dim=64, page_size=256, max_pages_per_seq=64)
+    ws = lib_workspace(lib, k2, 64)
+    assert lib.santa_value_sampled_workspace_size(ctypes.byref(k2), 64, ctypes.byref(n)) == OK and n.value > ws
+    assert call(ctypes.byref(k2), F, F, 64, 0, 32, 0, 1, 2, F, F, None, None, None, F, ws, None) == WS
+
+
+def lib_workspace(lib, k, M):
+    n = ctypes.c_size_t(0)
+    assert lib.santa_workspace_size(ctypes.byref(k), M, ctypes.byref(n)) == OK
+    return n.value
 
 
 def test_append_kv_validation(lib):
