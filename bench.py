@@ -105,6 +105,29 @@ def algorithmic_bytes(w, stats):
                 frac_head=head_reads / dense_head_reads, frac_hbm=(attend + select) / dense)
 
 
+def value_sampled_bytes(w, stats, positions):
+    """Bytes of the value-sampled call beyond the selection: the keys of every
+    union team once per (b, g), and the values of the distinct sampled tokens
+    of the group (row grain: d values per token), plus queries and outputs.
+    Also the value bytes at the cache's grain (a sampled token's values lie
+    across its 32-token chunk of the tile, [channel][token]) and the
+    per-query-head fraction of the dense bytes (keys of the head's drawn
+    teams, representatives, values of its distinct sampled tokens)."""
+    e, d, G, T = w.elem_bytes, w.head_dim, w.group, w.page_size
+    C = min(T, 32)
+    total = chunk_v = head_reads = dense_head_reads = 0
+    for b, g, L, K, u, per_head in stats:
+        pos_g = set()
+        for i, s in enumerate(per_head):
+            ph = set(int(x) for x in positions[b, g * G + i] if x >= 0)
+            pos_g |= ph
+            head_reads += K * d * e + sum(team_tokens(L, T, t) * d * e for t in s) + len(ph) * d * e
+            dense_head_reads += 2 * L * d * e
+        total += sum(team_tokens(L, T, t) * d * e for t in u) + len(pos_g) * d * e + G * d * e + G * (d + 1) * 4
+        chunk_v += len(set(x // C for x in pos_g)) * C * d * e
+    return dict(step=total, chunk_v=chunk_v, frac_head=head_reads / dense_head_reads)
+
+
 def time_stream(fn, steps, warmup, torch):
     """Eager launches: HIP events around ``steps`` calls (includes host launch cost if it dominates)."""
     for i in range(warmup):
@@ -325,7 +348,7 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
     torch.cuda.synchronize()
     r["attend_us"], _ = median_graph(attend_step, R, steps, warmup, torch)
 
-    r["schemes"], r["hashed"], r["kmeans"] = None, None, None
+    r["schemes"], r["hashed"], r["kmeans"], r["value_sampled"] = None, None, None, None
     if extras:
         # The variance-reduced draw schemes: whole decode call, and the bytes of
         # their (larger: fewer repeated teams) unions.
@@ -407,6 +430,37 @@ def measure(w, steps, warmup, layers, torch, S, calibrate=False, extras=True):
         kreps, ks_us, kfrac = santa_on(kcache)
 
         dense_out, _ = S.dense_decode_attention(kv0, q, wss[0])
+
+        # Value samples inside the drawn teams, S per head: the whole call,
+        # its bytes and the estimate's error against dense attention (as
+        # below, over 16 draw offsets).
+        vws = S.make_value_sampled_workspace(kv0, M)
+        r["value_sampled"] = {}
+        for Sn in (64, 256):
+            _, _, smp, _, pos = S.santa_decode_attention_value_sampled(
+                kv0, q, reps[0], M, Sn, seed=w.seed, offset=w.offset, workspace=vws, return_sets=True,
+                return_positions=True)
+            torch.cuda.synchronize()
+            vb = value_sampled_bytes(w, union_stats(w, smp.cpu().numpy()), pos.cpu().numpy())
+
+            def vs_step(i, Sn=Sn):
+                j = i % R
+                S.santa_decode_attention_value_sampled(cache[j], q, reps[j], M, Sn, seed=w.seed, offset=w.offset,
+                                                       workspace=vws, out=out, lse=lse)
+
+            us, _ = median_graph(vs_step, R, steps, warmup, torch)
+            verr = []
+            for off in range(16):
+                o, _ = S.santa_decode_attention_value_sampled(kv0, q, reps[0], M, Sn, seed=w.seed,
+                                                              offset=w.offset + 1000 + off, workspace=vws)
+                verr.append(((o - dense_out).norm(dim=-1) / dense_out.norm(dim=-1)).mean().item())
+            r["value_sampled"][str(Sn)] = {
+                "us_per_layer": round(us, 3), "bytes_row_grain": int(vb["step"] + ab["select"]),
+                "value_bytes_chunk_grain": int(vb["chunk_v"]),
+                "kv_read_fraction_per_query_head": round(vb["frac_head"], 4),
+                "estimate_rel_error": round(float(np.mean(verr)), 4)}
+        del vws
+
         errs = {"contiguous": [], "hashed": [], "kmeans": []}
         for off in range(16):
             for name, kv, rp in (("contiguous", kv0, reps[0]), ("hashed", hcache[0], hreps[0]),
@@ -508,6 +562,7 @@ def main():
         "draw_schemes": r["schemes"],
         "hashed_teams": r["hashed"],
         "kmeans_teams": r["kmeans"],
+        "value_sampled": r["value_sampled"],
         "roofline": {"kernel": "gather+combine (santa_attend_selected)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
@@ -528,7 +583,8 @@ def main():
                        "kv_read_fraction_hbm": round(a["frac_hbm"], 4), "team_mass": rs["mass"],
                        "build_reps_us": {k: round(v, 2) for k, v in rs["build_reps_us"].items()},
                        "draw_schemes": rs["schemes"],
-                       "hashed_teams": rs["hashed"], "kmeans_teams": rs["kmeans"]}
+                       "hashed_teams": rs["hashed"], "kmeans_teams": rs["kmeans"],
+                       "value_sampled": rs["value_sampled"]}
         del ws
         torch.cuda.empty_cache()
     if scale:

@@ -101,11 +101,11 @@ team-coherent keys both schemes lower the error. R11: code bits against
 basis directions, signs against exact rational dot products, a stable
 order that keeps separated clusters in one run, a per-head permutation
 that leaves dense attention unchanged, lower error on planted keys.
-R13-R14: the sample frequencies over an even grid of points equal the
-token probabilities, the mean over many offsets converges to the SANTA++
-estimate of the same teams, systematic samples give every token of mass
-at least k/S at least k samples, a one-token head returns its value, and
-the value stream differs from the team stream.
+R13-R14: given the teams, the mean over many offsets converges to the
+SANTA++ estimate of the same teams (and a planted oracle without the team
+weights does not), full coverage converges to dense attention, systematic
+points sample every drawn token floor(S p) or ceil(S p) times, a one-token
+head returns its value, and the value stream differs from the team stream.
 """
 import math
 from fractions import Fraction
