@@ -178,3 +178,46 @@ def test_value_sampled_full_size(name):
     torch.cuda.synchronize()
     assert np.array_equal(teams, t2.cpu().numpy())
     assert np.allclose(lse, l2.cpu().numpy(), rtol=0, atol=parity.LSE_TOL[w.dtype] + 1e-6 * np.abs(lse).max())
+
+
+def _random_configs(n=16, seed=4242):
+    """Shapes drawn from one seed: cache type, head dim, team size, group
+    size, batch, ragged lengths from one token, M (kept to at most 16384 drawn
+    tokens per head), S from 1 to 256, both schemes."""
+    rng = np.random.default_rng(seed)
+    schemes = ["iid", "systematic", "stratified"]
+    out = []
+    for i in range(n):
+        T = int(rng.choice([16, 32, 64, 128, 256]))
+        hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 3, 5, 7, 8, 16]))
+        if rng.random() < 0.3:
+            len_max, len_min = int(rng.integers(1, 2 * T + 1)), 1
+        else:
+            len_max = int(rng.integers(1, max(1, 5000 // T) + 1)) * T + int(rng.integers(0, T))
+            len_min = int(rng.integers(1, len_max + 1))
+        out.append(dict(name=f"v{i:02d}", dtype=str(rng.choice(["bf16", "f32"])), T=T, d=int(rng.choice([64, 128])),
+                        hkv=hkv, hq=G * hkv, seqs=int(rng.integers(1, 6)), len_min=len_min, len_max=len_max,
+                        M=int(rng.integers(1, min(80, 16384 // T) + 1)), S=int(rng.integers(1, 257)),
+                        scheme=str(rng.choice(schemes)), value_scheme=str(rng.choice(schemes)),
+                        data_seed=int(rng.integers(0, 2 ** 31)), philox_seed=int(rng.integers(0, 2 ** 63)),
+                        offset=int(rng.integers(0, 2 ** 32))))
+    return out
+
+
+RANDOM = _random_configs()
+
+
+@pytest.mark.parametrize("cfg", RANDOM, ids=[c["name"] for c in RANDOM])
+def test_value_sampled_random_shapes(cfg):
+    w = W.paged_ragged(data_seed=cfg["data_seed"], num_seqs=cfg["seqs"], len_min=cfg["len_min"],
+                       len_max=cfg["len_max"], T=cfg["T"], M=cfg["M"], hq=cfg["hq"], hkv=cfg["hkv"], d=cfg["d"],
+                       dtype=cfg["dtype"], philox_seed=cfg["philox_seed"])
+    w = W.dataclasses.replace(w, offset=cfg["offset"])
+    say(f"[value_sampled random] {cfg}")
+    kv, q = S.kv_from_workload(w)
+    reps_gpu = S.santa_build_reps(kv)
+    res = run_vs(w, kv, q, reps_gpu, cfg["S"], cfg["scheme"], cfg["value_scheme"])
+    reps = parity.check_reps(w, reps_gpu)
+    flips = compare(w, res, cfg["S"], scheme=cfg["scheme"], value_scheme=cfg["value_scheme"], reps=reps)
+    assert flips <= max(MAX_SAMPLE_FLIPS, w.batch * w.num_q_heads // 50)
