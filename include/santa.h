@@ -325,12 +325,12 @@ santa_status santa_value_sampled_workspace_size(const santa_kv *kv, int32_t M, s
 
 /* SANTA++ team draws, then value samples inside the drawn teams ([ABS] for
  * the teams and their 1/pi weights; "Stochastic Sparse Attention for
- * Memory-Bound Inference" (the SANTA page), abstract: drawing token indices
- * from the post-softmax weights and averaging only their value rows
- * estimates the weighted value sum without bias, with stratified and
- * systematic points as lower-variance choices). The teams, their weights
- * and the optional sorted set are those of santa_select_teams_ex with
- * `scheme`. Over the drawn tokens, in team order then token order, the
+ * Memory-Bound Inference" (the SANTA page), abstract: token positions
+ * picked with probability equal to their attention weight, and the mean of
+ * their values, give an unbiased stand-in for the attention output; evenly
+ * spread (stratified or systematic) picks reduce its variance). The teams,
+ * their weights and the optional sorted set are those of
+ * santa_select_teams_ex with `scheme`. Over the drawn tokens, in team order then token order, the
  * weighted logits are l_g = q . k_g / sqrt(d) + log w_t (float64 scores,
  * w_t as stored by the selection: the float32 -log(pi_t)); with
  * e_g = exp(l_g - max l) and C their running sums, value sample k takes the

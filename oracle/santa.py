@@ -688,8 +688,9 @@ class ValueSampled:
 def value_sampled_head(kv, q_h, reps, b, h, num_q_heads, M, S, seed, offset, scheme=DRAW_IID,
                        value_scheme=DRAW_IID):
     """SANTA++ team draws, then S value samples inside the drawn teams (R13,
-    R14; [SANTA] abstract: sampling indices from the post-softmax weights and
-    averaging only those value rows estimates the weighted value sum).
+    R14; [SANTA] abstract: positions picked with probability equal to their
+    attention weight, then the mean of their values, stand in for the
+    attention output without bias).
 
     The drawn teams and weights are select_teams'. Over the drawn tokens in
     team order, then token order, the weighted logits are

@@ -6,10 +6,10 @@
 //         arXiv 2609.35629, abstract: the teams to read are drawn from the
 //         team scores and a drawn team's terms count 1/pi times.
 //   [SAN] "Stochastic Sparse Attention for Memory-Bound Inference" (the
-//         SANTA page), abstract: drawing token indices from the post-softmax
-//         weights and averaging only those value rows estimates the weighted
-//         value sum without bias; stratified and systematic points lower the
-//         variance.
+//         SANTA page), abstract: positions picked with probability equal to
+//         their attention weight, then the mean of their values, stand in for
+//         the attention output without bias; evenly spread (stratified or
+//         systematic) picks reduce the variance.
 //
 // After the selection kernel (bitmaps and log weights in the workspace), the
 // drawn tokens of a head, in team order then token order (drawn token g is
