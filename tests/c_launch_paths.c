@@ -102,6 +102,7 @@ int main(void) {
     run_shape(SANTA_F32, 2, 4, 2, 128, 64, 47, 9);
     run_shape(SANTA_F32, 16, 8, 2, 64, 16, 300, 50);
     run_shape(SANTA_F32, 1, 16, 1, 64, 256, 20, 40);         /* M above the team count */
+    run_shape(SANTA_BF16, 1, 8, 2, 128, 128, 17, 7);         /* the smoke check's shape */
     EXPECT(santa_stub_launches() > before);
     if (failures) return 1;
     printf("launch paths ok (%llu stub launches)\n", santa_stub_launches() - before);
