@@ -221,3 +221,91 @@ def test_value_sampled_random_shapes(cfg):
     reps = parity.check_reps(w, reps_gpu)
     flips = compare(w, res, cfg["S"], scheme=cfg["scheme"], value_scheme=cfg["value_scheme"], reps=reps)
     assert flips <= max(MAX_SAMPLE_FLIPS, w.batch * w.num_q_heads // 50)
+
+
+def test_value_samples_unbiased_given_the_teams():
+    """Over many offsets (each call draws its teams and its value samples
+    afresh), the value-sampled output minus SANTA++'s output for the same
+    offset (the same teams: the team stream is shared) averages to zero
+    within five standard errors, per element: given the teams, the value
+    samples are unbiased for SANTA++'s estimate (the oracle pins show that
+    the same check catches value samples drawn without the team weights)."""
+    w = W.qwen_planted(batch=2, seq_len=4000 + 37, T=64, M=12, hq=8, hkv=2, d=128, plants=3)
+    R, S_ = 2000, 16
+    say(f"[value_sampled unbiased] {w.name} calls={R} S={S_}")
+    kv, q = S.kv_from_workload(w)
+    reps = S.santa_build_reps(kv)
+    vws, ws = S.make_value_sampled_workspace(kv, w.M), S.make_workspace(kv, w.M)
+    B, Hq, d = w.batch, w.num_q_heads, w.head_dim
+    vout = torch.empty((R, B, Hq, d), dtype=torch.float32, device="cuda")
+    sout = torch.empty((R, B, Hq, d), dtype=torch.float32, device="cuda")
+    vteams = torch.empty((R, B, Hq, w.M), dtype=torch.int32, device="cuda")
+    steams = torch.empty((R, B, Hq, w.M), dtype=torch.int32, device="cuda")
+    vinv = torch.empty((B, Hq, w.M), dtype=torch.float32, device="cuda")
+    sinv = torch.empty((B, Hq, w.M), dtype=torch.float32, device="cuda")
+    for i in range(R):
+        out, _, t, _ = S.santa_decode_attention_value_sampled(kv, q, reps, w.M, S_, seed=w.seed, offset=i,
+                                                              workspace=vws, out=vout[i], return_sets=True)
+        vteams[i].copy_(t)
+        S.santa_select_teams(kv, q, reps, w.M, w.seed, i, ws, steams[i], sinv)
+        S.santa_attend_selected(kv, q, w.M, ws, sout[i])
+    torch.cuda.synchronize()
+    assert torch.equal(vteams, steams)
+    v, s = vout.double().cpu().numpy(), sout.double().cpu().numpy()
+
+    def zmax(diff):
+        se = diff.std(axis=0, ddof=1) / np.sqrt(diff.shape[0])
+        return float(np.max(np.abs(diff.mean(axis=0)) / np.maximum(se, 1e-300)))
+
+    z = zmax(v - s)
+    say(f"  max |z| over {B * Hq * d} elements: {z:.2f}")
+    assert z < 5.0
+
+
+def test_value_sampled_graph_replays_match_eager():
+    """The three launches captured in a HIP graph: every replay, with eager
+    work between replays, reproduces the eager outputs and positions bit for
+    bit."""
+    w = W.qwen_mixed_query(batch=2, seq_len=8192, M=32)
+    say(f"[value_sampled graph] {w.name}")
+    kv, q = S.kv_from_workload(w)
+    reps = S.santa_build_reps(kv)
+    vws = S.make_value_sampled_workspace(kv, w.M)
+    B, Hq, d = w.batch, w.num_q_heads, w.head_dim
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    teams = torch.empty((B, Hq, w.M), dtype=torch.int32, device="cuda")
+    inv_pi = torch.empty((B, Hq, w.M), dtype=torch.float32, device="cuda")
+    pos = torch.empty((B, Hq, 64), dtype=torch.int32, device="cuda")
+    lib = S.load()
+
+    def step():
+        desc = kv.desc()
+        st = lib.santa_decode_attention_value_sampled(
+            S.ctypes.byref(desc), S._ptr(q), S._ptr(reps), w.M, 0, 64, 1, w.seed, 7, S._ptr(out), S._ptr(lse),
+            S._ptr(teams), S._ptr(inv_pi), S._ptr(pos), S._ptr(vws), vws.numel(), S._stream())
+        assert st == 0
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, teams, inv_pi, pos)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        for t in (out, lse, inv_pi):
+            t.fill_(float("nan"))
+        teams.fill_(-7)
+        pos.fill_(-7)
+        S.santa_decode_attention_value_sampled(kv, q, reps, w.M, 64, offset=8 + r)     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((out, lse, teams, inv_pi, pos), ref):
+            assert torch.equal(got, want), f"replay {r} differs from the eager result"
